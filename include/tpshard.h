@@ -1,0 +1,209 @@
+/*
+ * tpshard.h — C ABI of libtpshard.so: one GPU's share of a Megatron-style
+ * tensor-parallel (TP) layer on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (pages, by title and section):
+ *   [TPSP]    hs-black, "张量并行与序列并行" (scaling-tensor-parallel):
+ *             "矩阵乘法的两种切法" (column- and row-parallel linear and their
+ *             backward), "MLP：先列后行，只通信一次" (GeLU / SwiGLU MLP shard),
+ *             "注意力：按头切，以及 GQA 的约束" (head-aligned split, fused-QKV
+ *             layout, bias rule), "GQA：KV 头比 query 头少".
+ *   [REVISIT] pufanyi, "ml-revisit-infra", "Tensor Parallel" (identities,
+ *             gradients, the head-count ValueError).
+ *   [SB6]     r00kie-liu, "Scaling Book 入门第 6 章：分片矩阵乘法", §6.1
+ *             (sharding notation, Pop Quiz).
+ *
+ * Conventions for every call below.
+ *   Layout:    all matrices are dense, row-major, contiguous (leading
+ *              dimension = number of columns). A linear layer is Y = X W with
+ *              X[N,k], W[k,n] ([TPSP] notation; N = b*s tokens).
+ *   Types:     "bf16" = bfloat16 bit patterns (2 bytes); "f32" = IEEE float.
+ *              Products accumulate in f32 on the MFMA units; bf16 outputs are
+ *              rounded to nearest even.
+ *   Pointers:  device pointers (hipMalloc'd or torch CUDA tensors), 16-byte
+ *              aligned. The caller owns every buffer; the library keeps no
+ *              pointer after the call returns and allocates nothing.
+ *   Sizes:     N (tokens) is any value >= 0 (N = 0 is a no-op). Model widths
+ *              (k, n, h, f, k_loc) must be positive multiples of 64.
+ *   Streams:   `stream` is a hipStream_t (NULL = the legacy default stream).
+ *              Work is enqueued asynchronously; no host synchronisation.
+ *              Faults in kernels surface at the caller's next synchronisation.
+ *   Errors:    arguments are validated before any launch; on failure nothing
+ *              is enqueued, a status != TP_OK is returned and a message is
+ *              kept in thread-local storage (tp_last_error). Calls are
+ *              re-entrant across threads and streams.
+ *   {U}:       an f32 output marked {U} is a partial sum ("unreduced" in
+ *              [TPSP]/[SB6] notation): the full result is the sum of the t
+ *              ranks' outputs. The exchange that sums them (an all-reduce) is
+ *              not part of one GPU's share; `accumulate = 1` adds into the
+ *              output instead of overwriting it, so t shards computed one
+ *              after another on one device sum in rank order.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, bad size or enum   */
+    TP_ERR_NOT_DIVISIBLE = 2, /* a divisibility rule of the sharding is broken */
+    TP_ERR_UNSUPPORTED = 3,   /* valid request outside what is implemented     */
+    TP_ERR_HIP = 4            /* the HIP runtime reported an error at launch   */
+} tp_status;
+
+typedef enum {
+    TP_ACT_NONE = 0,
+    TP_ACT_GELU = 1,   /* exact GeLU, x * Phi(x)                              */
+    TP_ACT_SWIGLU = 2  /* SiLU(gate) * up over [gate | up] weight halves      */
+} tp_act;
+
+/* Library version, (major << 16) | minor. */
+int tp_version(void);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char* tp_last_error(void);
+
+/*
+ * Column-parallel linear with its local activation ([TPSP] "矩阵乘法的两种切法",
+ * first identity; "MLP：先列后行" for the activation; [REVISIT] Column-wise TP).
+ * The rank holds the full X and the column block W_i; its output columns need
+ * no exchange.
+ *   X      bf16 [N, k]          input (replicated on every rank)
+ *   W      bf16 [k, n_w]        act NONE / GELU: n_w = n_out.
+ *                               act SWIGLU: n_w = 2*n_out, W = [W_gate | W_up],
+ *                               gate column j and up column j cover the same
+ *                               F index (same F segment on this rank).
+ *   Y      bf16 [N, n_out]      NONE: X W;  GELU: GeLU(X W);
+ *                               SWIGLU: SiLU(X W_gate) * (X W_up).
+ *   H_save bf16 [N, n_w] or NULL  receives the pre-activation X W (needed by
+ *                               the backward). Must be NULL for act NONE.
+ * Errors: INVALID_ARG (pointers, sizes, act), UNSUPPORTED (width not a
+ * multiple of 64), HIP.
+ */
+tp_status tp_col_linear(const void* X, const void* W, void* Y,
+                        int64_t N, int64_t k, int64_t n_out, int act,
+                        void* H_save, void* stream);
+
+/*
+ * Row-parallel linear, partial sum ([TPSP] "矩阵乘法的两种切法", second
+ * identity; [REVISIT] Row-wise TP). The rank holds the input slice
+ * Z_i[N, k_loc] and the weight row block W_i[k_loc, n]; Z_i W_i is a
+ * full-shape partial sum. No bias is ever added here: a row-parallel bias
+ * belongs after the exchange ([TPSP] attention section, bias item).
+ *   Z  bf16 [N, k_loc]   W  bf16 [k_loc, n]
+ *   P  f32  [N, n] {U}   P = Z W, or P += Z W when accumulate != 0.
+ */
+tp_status tp_row_linear_partial(const void* Z, const void* W, float* P,
+                                int64_t N, int64_t k_loc, int64_t n,
+                                int accumulate, void* stream);
+
+/*
+ * One rank's MLP share, forward ([TPSP] "MLP：先列后行，只通信一次"): first
+ * matrix column-split with the activation applied locally, second matrix
+ * row-split, giving the partial sum of the layer output.
+ *   X      bf16 [N, h]
+ *   W_in   bf16 [h, n_w]     GELU: n_w = f (A_i);  SWIGLU: n_w = 2f, [gate|up]
+ *   W_out  bf16 [f, h]       (B_i / W_down,i)
+ *   Z      bf16 [N, f]       activation output (input of the row-parallel GEMM,
+ *                            kept for the backward's dW_out)
+ *   H_save bf16 [N, n_w] or NULL   pre-activation (needed by the backward)
+ *   P      f32  [N, h] {U}   Z W_out (accumulate != 0: added into P)
+ * act must be GELU or SWIGLU. f = F/t is the per-rank MLP width.
+ */
+tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out,
+                           int64_t N, int64_t h, int64_t f, int act,
+                           void* Z, void* H_save, float* P, int accumulate,
+                           void* stream);
+
+/*
+ * One rank's MLP share, backward ([TPSP] "矩阵乘法的两种切法", backward
+ * paragraph, applied to the MLP; [REVISIT] gradients):
+ *   dZ     = dY W_out^T                          (row-parallel, local)
+ *   dH     = dZ through the activation:
+ *            GELU:   dA = dZ * GeLU'(A)
+ *            SWIGLU: dG = dZ * U * SiLU'(G),  dU = dZ * SiLU(G),  dH = [dG|dU]
+ *   dX_part = dH W_in^T         {U}              (column-parallel, partial)
+ *   dW_in   = X^T dH                              (local)
+ *   dW_out  = Z^T dY                              (local)
+ * Inputs: X bf16 [N,h], W_in bf16 [h,n_w], W_out bf16 [f,h], H_save bf16
+ * [N,n_w] (the forward's pre-activation, required), Z bf16 [N,f] (the forward's
+ * activation output, required), dY bf16 [N,h].
+ * Outputs: dH bf16 [N,n_w] (also the caller-owned workspace of the two
+ * GEMMs that follow), dX_part f32 [N,h] {U} (accumulate != 0 adds into it),
+ * dW_in f32 [h,n_w], dW_out f32 [f,h]. dZ itself is never stored.
+ */
+tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out,
+                           const void* H_save, const void* Z, const void* dY,
+                           int64_t N, int64_t h, int64_t f, int act,
+                           void* dH, float* dX_part, float* dW_in, float* dW_out,
+                           int accumulate, void* stream);
+
+/*
+ * Column-parallel linear, backward ([TPSP] "矩阵乘法的两种切法": dX is a partial
+ * sum over ranks, dW_i is local). Used for the fused-QKV projection.
+ *   X bf16 [N,k], W bf16 [k,n], dY bf16 [N,n]
+ *   dX_part f32 [N,k] {U} = dY W^T (NULL: skipped; accumulate != 0 adds)
+ *   dW      f32 [k,n]     = X^T dY (NULL: skipped)
+ */
+tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY,
+                            float* dX_part, float* dW,
+                            int64_t N, int64_t k, int64_t n, int accumulate,
+                            void* stream);
+
+/*
+ * Row-parallel linear, backward ([TPSP] "矩阵乘法的两种切法": both gradients are
+ * local). Used for the attention output projection W_O.
+ *   Z bf16 [N,k_loc], W bf16 [k_loc,n], dY bf16 [N,n]
+ *   dZ bf16 [N,k_loc] = dY W^T (NULL: skipped)
+ *   dW f32  [k_loc,n] = Z^T dY (NULL: skipped)
+ */
+tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY,
+                            void* dZ, float* dW,
+                            int64_t N, int64_t k_loc, int64_t n, void* stream);
+
+/*
+ * Per-rank regroup of the fused QKV weight ([TPSP] attention section, fused
+ * QKV item: an equal column split is wrong; each rank's slice must hold its
+ * own Q heads, then its own K heads, then its own V heads; "GQA" section:
+ * t | n_kv keeps each query group with its KV head).
+ *   W_qkv bf16 [h, (n_h + 2 n_kv) d_h] = [Q heads 0..n_h-1 | K heads 0..n_kv-1
+ *         | V heads 0..n_kv-1], each head's d_h columns contiguous.
+ *   W_r   bf16 [h, (n_h + 2 n_kv) d_h / t] = [Q heads r n_h/t .. (r+1) n_h/t - 1
+ *         | K heads r n_kv/t .. | V heads r n_kv/t ..].
+ * A bit-exact copy. Errors: NOT_DIVISIBLE when t does not divide n_h
+ * (message in Megatron's wording, [REVISIT]); UNSUPPORTED when t does not
+ * divide n_kv (KV-head replication for n_kv < t is not implemented);
+ * INVALID_ARG for rank outside [0, t), d_h not a multiple of 8, bad pointers.
+ */
+tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h,
+                         int32_t n_h, int32_t n_kv, int32_t d_h,
+                         int32_t t, int32_t rank, void* stream);
+
+/*
+ * Shard arithmetic of a tensor over a device mesh ([SB6] §6.1): host only,
+ * no device work. A[I_{XY}, J] splits dim I over mesh axes X and Y (divided
+ * by their product); axes no dim uses replicate the shard.
+ *   shape[ndim], elem_bytes > 0, axis_sizes[n_axes] (n_axes <= 32),
+ *   dim_axis_mask[ndim]: bit a set = dim is split over mesh axis a.
+ * Outputs: local_shape_out[ndim], *local_bytes_out, *total_bytes_out
+ * (= local bytes times the number of devices, the product of axis sizes).
+ * Errors: INVALID_ARG when one mesh axis splits two dims (A[I_X, J_X] is
+ * illegal) or for bad arguments; NOT_DIVISIBLE when a dim does not divide.
+ */
+tp_status tp_shard_shape(int32_t ndim, const int64_t* shape, int32_t elem_bytes,
+                         int32_t n_axes, const int64_t* axis_sizes,
+                         const uint32_t* dim_axis_mask,
+                         int64_t* local_shape_out, int64_t* local_bytes_out,
+                         int64_t* total_bytes_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

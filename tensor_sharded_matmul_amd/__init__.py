@@ -1,0 +1,271 @@
+"""Python binding of libtpshard.so (one GPU's share of a tensor-parallel layer).
+
+Argument marshalling only: every function checks dtypes, devices, shapes and
+contiguity of torch tensors, passes their device pointers and the current
+torch stream to the C entry point of the same name (include/tpshard.h), and
+allocates missing outputs with torch. All arithmetic runs in the HIP kernels
+of libtpshard.so; there is no fallback: if the library is not built, or no
+GPU is present, the calls raise.
+
+Errors: INVALID_ARG / NOT_DIVISIBLE -> ValueError, UNSUPPORTED ->
+NotImplementedError, HIP -> RuntimeError (message from tp_last_error).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib_path", "load", "tp_version", "tp_last_error", "tp_col_linear",
+    "tp_row_linear_partial", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+    "tp_col_linear_bwd", "tp_row_linear_bwd", "tp_qkv_regroup", "tp_shard_shape",
+    "ACT", "TPError",
+]
+
+ACT = {"none": 0, "gelu": 1, "swiglu": 2}
+_STATUS = {0: "TP_OK", 1: "TP_ERR_INVALID_ARG", 2: "TP_ERR_NOT_DIVISIBLE",
+           3: "TP_ERR_UNSUPPORTED", 4: "TP_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class TPError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libtpshard.so")
+
+
+def load():
+    """Load libtpshard.so (torch is imported first so both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m tensor_sharded_matmul_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sigs = {
+        "tp_version": ([], ctypes.c_int),
+        "tp_last_error": ([], ctypes.c_char_p),
+        "tp_col_linear": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp], ctypes.c_int),
+        "tp_row_linear_partial": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp], ctypes.c_int),
+        "tp_mlp_shard_fwd": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp],
+                             ctypes.c_int),
+        "tp_mlp_shard_bwd": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
+                              ctypes.c_int, vp], ctypes.c_int),
+        "tp_col_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp], ctypes.c_int),
+        "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
+        "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+        "tp_shard_shape": ([i32, ctypes.POINTER(i64), i32, i32, ctypes.POINTER(i64),
+                            ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64),
+                            ctypes.POINTER(i64), ctypes.POINTER(i64)], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status == 0:
+        return
+    msg = load().tp_last_error().decode(errors="replace")
+    name = _STATUS.get(status, str(status))
+    if status in (1, 2):
+        raise ValueError(f"{name}: {msg}")
+    if status == 3:
+        raise NotImplementedError(f"{name}: {msg}")
+    raise TPError(f"{name}: {msg}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, name, dtype, shape, like):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _dev(t, name, dtype, shape)
+
+
+_bf16, _f32 = torch.bfloat16, torch.float32
+
+
+def tp_version() -> int:
+    return load().tp_version()
+
+
+def tp_last_error() -> str:
+    return load().tp_last_error().decode(errors="replace")
+
+
+def tp_col_linear(X, W, act="none", Y=None, H_save=None, want_h=False, stream=None):
+    """Y = act(X W) (SwiGLU: W = [gate | up]); returns (Y, H_save or None)."""
+    lib = load()
+    a = ACT[act]
+    N, k = X.shape
+    n_w = W.shape[1]
+    n_out = n_w // 2 if act == "swiglu" else n_w
+    _dev(X, "X", _bf16, (N, k))
+    _dev(W, "W", _bf16, (k, n_w))
+    Y = _out(Y, "Y", _bf16, (N, n_out), X)
+    if want_h and H_save is None and act != "none":
+        H_save = torch.empty((N, n_w), dtype=_bf16, device=X.device)
+    if H_save is not None:
+        _dev(H_save, "H_save", _bf16, (N, n_w))
+    _check(lib.tp_col_linear(_ptr(X), _ptr(W), _ptr(Y), N, k, n_out, a, _ptr(H_save),
+                             _stream(stream)))
+    return Y, H_save
+
+
+def tp_row_linear_partial(Z, W, P=None, accumulate=False, stream=None):
+    """P = Z W (or P += Z W), f32 partial sum; returns P."""
+    lib = load()
+    N, k_loc = Z.shape
+    n = W.shape[1]
+    _dev(Z, "Z", _bf16, (N, k_loc))
+    _dev(W, "W", _bf16, (k_loc, n))
+    P = _out(P, "P", _f32, (N, n), Z)
+    _check(lib.tp_row_linear_partial(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
+                                     _stream(stream)))
+    return P
+
+
+def tp_mlp_shard_fwd(X, W_in, W_out, act, Z=None, H_save=None, P=None, want_h=True,
+                     accumulate=False, stream=None):
+    """One rank's MLP forward; returns (Z, H_save or None, P)."""
+    lib = load()
+    a = ACT[act]
+    N, h = X.shape
+    f = W_out.shape[0]
+    n_w = 2 * f if act == "swiglu" else f
+    _dev(X, "X", _bf16, (N, h))
+    _dev(W_in, "W_in", _bf16, (h, n_w))
+    _dev(W_out, "W_out", _bf16, (f, h))
+    Z = _out(Z, "Z", _bf16, (N, f), X)
+    if want_h and H_save is None:
+        H_save = torch.empty((N, n_w), dtype=_bf16, device=X.device)
+    if H_save is not None:
+        _dev(H_save, "H_save", _bf16, (N, n_w))
+    P = _out(P, "P", _f32, (N, h), X)
+    _check(lib.tp_mlp_shard_fwd(_ptr(X), _ptr(W_in), _ptr(W_out), N, h, f, a, _ptr(Z), _ptr(H_save),
+                                _ptr(P), int(bool(accumulate)), _stream(stream)))
+    return Z, H_save, P
+
+
+def tp_mlp_shard_bwd(X, W_in, W_out, H_save, Z, dY, act, dH=None, dX_part=None, dW_in=None,
+                     dW_out=None, accumulate=False, stream=None):
+    """One rank's MLP backward; returns (dH, dX_part, dW_in, dW_out)."""
+    lib = load()
+    a = ACT[act]
+    N, h = X.shape
+    f = W_out.shape[0]
+    n_w = 2 * f if act == "swiglu" else f
+    _dev(X, "X", _bf16, (N, h))
+    _dev(W_in, "W_in", _bf16, (h, n_w))
+    _dev(W_out, "W_out", _bf16, (f, h))
+    _dev(H_save, "H_save", _bf16, (N, n_w))
+    _dev(Z, "Z", _bf16, (N, f))
+    _dev(dY, "dY", _bf16, (N, h))
+    dH = _out(dH, "dH", _bf16, (N, n_w), X)
+    dX_part = _out(dX_part, "dX_part", _f32, (N, h), X)
+    dW_in = _out(dW_in, "dW_in", _f32, (h, n_w), X)
+    dW_out = _out(dW_out, "dW_out", _f32, (f, h), X)
+    _check(lib.tp_mlp_shard_bwd(_ptr(X), _ptr(W_in), _ptr(W_out), _ptr(H_save), _ptr(Z), _ptr(dY),
+                                N, h, f, a, _ptr(dH), _ptr(dX_part), _ptr(dW_in), _ptr(dW_out),
+                                int(bool(accumulate)), _stream(stream)))
+    return dH, dX_part, dW_in, dW_out
+
+
+def tp_col_linear_bwd(X, W, dY, dX_part=None, dW=None, want_dx=True, want_dw=True,
+                      accumulate=False, stream=None):
+    """dX_part = dY W^T ({U}), dW = X^T dY; returns (dX_part, dW)."""
+    lib = load()
+    N, k = X.shape
+    n = W.shape[1]
+    _dev(X, "X", _bf16, (N, k))
+    _dev(W, "W", _bf16, (k, n))
+    _dev(dY, "dY", _bf16, (N, n))
+    if want_dx:
+        dX_part = _out(dX_part, "dX_part", _f32, (N, k), X)
+    if want_dw:
+        dW = _out(dW, "dW", _f32, (k, n), X)
+    _check(lib.tp_col_linear_bwd(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX_part if want_dx else None),
+                                 _ptr(dW if want_dw else None), N, k, n, int(bool(accumulate)),
+                                 _stream(stream)))
+    return (dX_part if want_dx else None), (dW if want_dw else None)
+
+
+def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, stream=None):
+    """dZ = dY W^T (bf16), dW = Z^T dY (f32); returns (dZ, dW)."""
+    lib = load()
+    N, k_loc = Z.shape
+    n = W.shape[1]
+    _dev(Z, "Z", _bf16, (N, k_loc))
+    _dev(W, "W", _bf16, (k_loc, n))
+    _dev(dY, "dY", _bf16, (N, n))
+    if want_dz:
+        dZ = _out(dZ, "dZ", _bf16, (N, k_loc), Z)
+    if want_dw:
+        dW = _out(dW, "dW", _f32, (k_loc, n), Z)
+    _check(lib.tp_row_linear_bwd(_ptr(Z), _ptr(W), _ptr(dY), _ptr(dZ if want_dz else None),
+                                 _ptr(dW if want_dw else None), N, k_loc, n, _stream(stream)))
+    return (dZ if want_dz else None), (dW if want_dw else None)
+
+
+def tp_qkv_regroup(W_qkv, n_h, n_kv, d_h, t, rank, W_r=None, stream=None):
+    """Rank-local [Q_r | K_r | V_r] columns of the fused QKV weight; returns W_r."""
+    lib = load()
+    h, width = W_qkv.shape
+    if width != (n_h + 2 * n_kv) * d_h:
+        raise ValueError(f"W_qkv width {width} != (n_h + 2 n_kv) d_h = {(n_h + 2 * n_kv) * d_h}")
+    _dev(W_qkv, "W_qkv", _bf16, (h, width))
+    out_w = width // t if t > 0 and width % t == 0 else 0
+    if W_r is None:
+        W_r = torch.empty((h, out_w), dtype=_bf16, device=W_qkv.device)
+    else:
+        _dev(W_r, "W_r", _bf16, (h, out_w))
+    _check(lib.tp_qkv_regroup(_ptr(W_qkv), _ptr(W_r), h, n_h, n_kv, d_h, t, rank, _stream(stream)))
+    return W_r
+
+
+def tp_shard_shape(shape, elem_bytes, axis_sizes, dim_axis_mask):
+    """Host-only shard arithmetic; returns (local_shape, local_bytes, total_bytes)."""
+    lib = load()
+    nd, na = len(shape), len(axis_sizes)
+    I64 = ctypes.c_int64
+    sh = (I64 * max(nd, 1))(*shape)
+    ax = (I64 * max(na, 1))(*axis_sizes)
+    mk = (ctypes.c_uint32 * max(nd, 1))(*dim_axis_mask)
+    loc = (I64 * max(nd, 1))()
+    lb, tb = I64(), I64()
+    _check(lib.tp_shard_shape(nd, sh, elem_bytes, na, ax, mk, loc, ctypes.byref(lb), ctypes.byref(tb)))
+    return tuple(loc[i] for i in range(nd)), lb.value, tb.value

@@ -1,0 +1,426 @@
+// tpshard.hip — host side of libtpshard.so: argument validation, kernel
+// selection and launch for every entry point declared in include/tpshard.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/tpshard.h"
+#include "gemm_kernel.h"
+
+namespace tps {
+
+// ---------------------------------------------------------------------------
+// Errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+static tp_status fail(tp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+static tp_status ok() {
+    g_last_error.clear();
+    return TP_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define TP_CHECK_PTR(p, name)                                                             \
+    do {                                                                                  \
+        if ((p) == nullptr) return fail(TP_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);  \
+        if (!aligned16(p))                                                                \
+            return fail(TP_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);   \
+    } while (0)
+
+// Token-sized buffers ([N, *]) may be NULL when N == 0 (an empty torch tensor).
+#define TP_CHECK_TOK_PTR(p, name)                                                         \
+    do {                                                                                  \
+        if (N != 0) TP_CHECK_PTR(p, name);                                                \
+        else TP_CHECK_OPT_PTR(p, name);                                                   \
+    } while (0)
+
+#define TP_CHECK_OPT_PTR(p, name)                                                         \
+    do {                                                                                  \
+        if ((p) != nullptr && !aligned16(p))                                              \
+            return fail(TP_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);   \
+    } while (0)
+
+static tp_status check_tokens(const char* fn, int64_t N) {
+    if (N < 0) return fail(TP_ERR_INVALID_ARG, "%s: N = %lld < 0", fn, (long long)N);
+    if (N > (int64_t)1 << 30) return fail(TP_ERR_UNSUPPORTED, "%s: N = %lld too large", fn, (long long)N);
+    return TP_OK;
+}
+
+static tp_status check_width(const char* fn, const char* name, int64_t v) {
+    if (v <= 0) return fail(TP_ERR_INVALID_ARG, "%s: %s = %lld must be positive", fn, name, (long long)v);
+    if (v % 64 != 0)
+        return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld is not a multiple of 64", fn, name, (long long)v);
+    if (v > (int64_t)1 << 24) return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld too large", fn, name, (long long)v);
+    return TP_OK;
+}
+
+// Element offsets of every operand must fit the kernels' 32-bit row indices
+// times a 64-bit stride; the product itself is formed in size_t.
+static tp_status check_elems(const char* fn, int64_t rows, int64_t cols) {
+    if (rows * cols > ((int64_t)1 << 40)) return fail(TP_ERR_UNSUPPORTED, "%s: operand too large", fn);
+    return TP_OK;
+}
+
+#define TP_TRY(expr)                      \
+    do {                                  \
+        tp_status _st = (expr);           \
+        if (_st != TP_OK) return _st;     \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// GEMM dispatch
+// ---------------------------------------------------------------------------
+enum Layout { NN, NT, TN };
+
+template <int BM, int BN, bool A_T, bool B_KN, int EPI>
+static tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
+    constexpr int BNZ = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + BNZ - 1) / BNZ);
+    if (tiles == 0) return TP_OK;
+    if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, A_T, B_KN, EPI>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return TP_OK;
+}
+
+template <bool A_T, bool B_KN, int EPI>
+static tp_status launch_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0) return TP_OK;
+    // Large problems: 256x256 tiles (128x128 per wave). Few rows: 64x128.
+    if (a.M >= 256 || A_T) return launch_cfg<256, 256, A_T, B_KN, EPI>(fn, a, s);
+    return launch_cfg<64, 128, A_T, B_KN, EPI>(fn, a, s);
+}
+
+static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb,
+                          int ldc) {
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    return a;
+}
+
+// ---------------------------------------------------------------------------
+// Fused-QKV regroup: a bit-exact gather of three contiguous column runs per
+// row, 16 bytes per thread, output written in order (fully coalesced).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) qkv_regroup_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int64_t h,
+                                                          int src_w, int q_w, int kv_w, int q_src0,
+                                                          int k_src0, int v_src0) {
+    const int out_w = q_w + 2 * kv_w;
+    const int chunks_per_row = out_w >> 3;
+    const int64_t total = h * chunks_per_row;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = c / chunks_per_row;
+        const int col = (int)(c - row * chunks_per_row) << 3;
+        int scol;
+        if (col < q_w) {
+            scol = q_src0 + col;
+        } else if (col < q_w + kv_w) {
+            scol = k_src0 + (col - q_w);
+        } else {
+            scol = v_src0 + (col - q_w - kv_w);
+        }
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + row * src_w + scol);
+        *reinterpret_cast<u32x4_t*>(dst + row * out_w + col) = v;
+    }
+}
+
+}  // namespace tps
+
+using namespace tps;
+
+extern "C" {
+
+int tp_version(void) { return (0 << 16) | 1; }
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_t k, int64_t n_out,
+                        int act, void* H_save, void* stream) {
+    const char* fn = "tp_col_linear";
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k", k));
+    TP_TRY(check_width(fn, "n_out", n_out));
+    if (act != TP_ACT_NONE && act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+        return fail(TP_ERR_INVALID_ARG, "%s: unknown act %d", fn, act);
+    if (act == TP_ACT_NONE && H_save != nullptr)
+        return fail(TP_ERR_INVALID_ARG, "%s: H_save must be NULL for act NONE", fn);
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(Y, "Y");
+    TP_CHECK_OPT_PTR(H_save, "H_save");
+    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * n_out : n_out;
+    TP_TRY(check_elems(fn, N, k));
+    TP_TRY(check_elems(fn, k, n_w));
+    TP_TRY(check_elems(fn, N, n_w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GemmArgs a = make_args(X, W, Y, (int)N, (int)n_out, (int)k, (int)k, (int)n_w, (int)n_out);
+    a.C2 = static_cast<uint16_t*>(H_save);
+    a.ldc2 = (int)n_w;
+    a.f = (int)n_out;
+    tp_status st;
+    if (act == TP_ACT_NONE) st = launch_gemm<false, true, EPI_BF16>(fn, a, s);
+    else if (act == TP_ACT_GELU) st = launch_gemm<false, true, EPI_GELU>(fn, a, s);
+    else st = launch_gemm<false, true, EPI_SWIGLU>(fn, a, s);
+    return st == TP_OK ? ok() : st;
+}
+
+tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc, int64_t n,
+                                int accumulate, void* stream) {
+    const char* fn = "tp_row_linear_partial";
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k_loc", k_loc));
+    TP_TRY(check_width(fn, "n", n));
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(P, "P");
+    TP_TRY(check_elems(fn, N, k_loc));
+    TP_TRY(check_elems(fn, k_loc, n));
+    TP_TRY(check_elems(fn, N, n));
+    GemmArgs a = make_args(Z, W, P, (int)N, (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
+    a.accumulate = accumulate ? 1 : 0;
+    tp_status st = launch_gemm<false, true, EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
+    return st == TP_OK ? ok() : st;
+}
+
+tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, int64_t N, int64_t h,
+                           int64_t f, int act, void* Z, void* H_save, float* P, int accumulate,
+                           void* stream) {
+    const char* fn = "tp_mlp_shard_fwd";
+    if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+        return fail(TP_ERR_INVALID_ARG, "%s: act must be GELU or SWIGLU (got %d)", fn, act);
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "f", f));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W_in, "W_in");
+    TP_CHECK_PTR(W_out, "W_out");
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_TOK_PTR(P, "P");
+    TP_CHECK_OPT_PTR(H_save, "H_save");
+    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, n_w));
+    TP_TRY(check_elems(fn, N, n_w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GemmArgs a = make_args(X, W_in, Z, (int)N, (int)f, (int)h, (int)h, (int)n_w, (int)f);
+    a.C2 = static_cast<uint16_t*>(H_save);
+    a.ldc2 = (int)n_w;
+    a.f = (int)f;
+    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, true, EPI_GELU>(fn, a, s)
+                                      : launch_gemm<false, true, EPI_SWIGLU>(fn, a, s);
+    if (st != TP_OK) return st;
+    GemmArgs b = make_args(Z, W_out, P, (int)N, (int)h, (int)f, (int)f, (int)h, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    st = launch_gemm<false, true, EPI_F32>(fn, b, s);
+    return st == TP_OK ? ok() : st;
+}
+
+tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out, const void* H_save,
+                           const void* Z, const void* dY, int64_t N, int64_t h, int64_t f, int act,
+                           void* dH, float* dX_part, float* dW_in, float* dW_out, int accumulate,
+                           void* stream) {
+    const char* fn = "tp_mlp_shard_bwd";
+    if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+        return fail(TP_ERR_INVALID_ARG, "%s: act must be GELU or SWIGLU (got %d)", fn, act);
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "f", f));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W_in, "W_in");
+    TP_CHECK_PTR(W_out, "W_out");
+    TP_CHECK_TOK_PTR(H_save, "H_save");
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_TOK_PTR(dY, "dY");
+    TP_CHECK_TOK_PTR(dH, "dH");
+    TP_CHECK_TOK_PTR(dX_part, "dX_part");
+    TP_CHECK_PTR(dW_in, "dW_in");
+    TP_CHECK_PTR(dW_out, "dW_out");
+    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, n_w));
+    TP_TRY(check_elems(fn, N, n_w));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // dZ = dY W_out^T (NT) with the activation backward in the epilogue -> dH
+    GemmArgs a = make_args(dY, W_out, dH, (int)N, (int)f, (int)h, (int)h, (int)h, (int)n_w);
+    a.aux = static_cast<const uint16_t*>(H_save);
+    a.ldc2 = (int)n_w;
+    a.f = (int)f;
+    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, false, EPI_GELU_BWD>(fn, a, s)
+                                      : launch_gemm<false, false, EPI_SWIGLU_BWD>(fn, a, s);
+    if (st != TP_OK) return st;
+    // dX_part = dH W_in^T (NT)
+    GemmArgs b = make_args(dH, W_in, dX_part, (int)N, (int)h, (int)n_w, (int)n_w, (int)n_w, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    st = launch_gemm<false, false, EPI_F32>(fn, b, s);
+    if (st != TP_OK) return st;
+    // dW_in = X^T dH (TN): A = X stored [K=N][M=h], B = dH stored [K=N][n_w]
+    GemmArgs c = make_args(X, dH, dW_in, (int)h, (int)n_w, (int)N, (int)h, (int)n_w, (int)n_w);
+    st = launch_gemm<true, true, EPI_F32>(fn, c, s);
+    if (st != TP_OK) return st;
+    // dW_out = Z^T dY (TN): A = Z stored [N][f], B = dY stored [N][h]
+    GemmArgs d = make_args(Z, dY, dW_out, (int)f, (int)h, (int)N, (int)f, (int)h, (int)h);
+    st = launch_gemm<true, true, EPI_F32>(fn, d, s);
+    return st == TP_OK ? ok() : st;
+}
+
+tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY, float* dX_part, float* dW,
+                            int64_t N, int64_t k, int64_t n, int accumulate, void* stream) {
+    const char* fn = "tp_col_linear_bwd";
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k", k));
+    TP_TRY(check_width(fn, "n", n));
+    TP_CHECK_TOK_PTR(dY, "dY");
+    TP_CHECK_OPT_PTR(dX_part, "dX_part");
+    TP_CHECK_OPT_PTR(dW, "dW");
+    if (dX_part) TP_CHECK_PTR(W, "W");
+    if (dW) TP_CHECK_TOK_PTR(X, "X");
+    TP_TRY(check_elems(fn, N, k));
+    TP_TRY(check_elems(fn, k, n));
+    TP_TRY(check_elems(fn, N, n));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dX_part) {
+        GemmArgs a = make_args(dY, W, dX_part, (int)N, (int)k, (int)n, (int)n, (int)n, (int)k);
+        a.accumulate = accumulate ? 1 : 0;
+        TP_TRY((launch_gemm<false, false, EPI_F32>(fn, a, s)));
+    }
+    if (dW) {
+        GemmArgs b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
+        TP_TRY((launch_gemm<true, true, EPI_F32>(fn, b, s)));
+    }
+    return ok();
+}
+
+tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY, void* dZ, float* dW, int64_t N,
+                            int64_t k_loc, int64_t n, void* stream) {
+    const char* fn = "tp_row_linear_bwd";
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k_loc", k_loc));
+    TP_TRY(check_width(fn, "n", n));
+    TP_CHECK_TOK_PTR(dY, "dY");
+    TP_CHECK_OPT_PTR(dZ, "dZ");
+    TP_CHECK_OPT_PTR(dW, "dW");
+    if (dZ) TP_CHECK_PTR(W, "W");
+    if (dW) TP_CHECK_TOK_PTR(Z, "Z");
+    TP_TRY(check_elems(fn, N, k_loc));
+    TP_TRY(check_elems(fn, k_loc, n));
+    TP_TRY(check_elems(fn, N, n));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dZ) {
+        GemmArgs a = make_args(dY, W, dZ, (int)N, (int)k_loc, (int)n, (int)n, (int)n, (int)k_loc);
+        TP_TRY((launch_gemm<false, false, EPI_BF16>(fn, a, s)));
+    }
+    if (dW) {
+        GemmArgs b = make_args(Z, dY, dW, (int)k_loc, (int)n, (int)N, (int)k_loc, (int)n, (int)n);
+        TP_TRY((launch_gemm<true, true, EPI_F32>(fn, b, s)));
+    }
+    return ok();
+}
+
+tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h, int32_t n_h, int32_t n_kv, int32_t d_h,
+                         int32_t t, int32_t rank, void* stream) {
+    const char* fn = "tp_qkv_regroup";
+    if (t <= 0) return fail(TP_ERR_INVALID_ARG, "%s: TP degree t = %d must be positive", fn, t);
+    if (n_h <= 0 || n_kv <= 0 || d_h <= 0)
+        return fail(TP_ERR_INVALID_ARG, "%s: head counts and head width must be positive", fn);
+    if (n_h % t != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE,
+                    "%s: num_attention_heads (%d) must be a multiple of tensor_model_parallel_size (%d).",
+                    fn, n_h, t);
+    if (n_kv % t != 0)
+        return fail(TP_ERR_UNSUPPORTED,
+                    "%s: num_kv_heads (%d) is not a multiple of the TP degree (%d); KV-head replication "
+                    "is not implemented",
+                    fn, n_kv, t);
+    if (rank < 0 || rank >= t) return fail(TP_ERR_INVALID_ARG, "%s: rank %d outside [0, %d)", fn, rank, t);
+    if (d_h % 8 != 0) return fail(TP_ERR_INVALID_ARG, "%s: d_h = %d must be a multiple of 8", fn, d_h);
+    if (h < 0) return fail(TP_ERR_INVALID_ARG, "%s: h = %lld < 0", fn, (long long)h);
+    const int64_t src_w64 = (int64_t)(n_h + 2 * n_kv) * d_h;
+    if (src_w64 > 0x7fffffff) return fail(TP_ERR_UNSUPPORTED, "%s: fused width too large", fn);
+    if (h == 0) return ok();
+    TP_CHECK_PTR(W_qkv, "W_qkv");
+    TP_CHECK_PTR(W_r, "W_r");
+    const int q_w = n_h / t * d_h;
+    const int kv_w = n_kv / t * d_h;
+    const int src_w = (int)src_w64;
+    const int q_src0 = rank * q_w;
+    const int k_src0 = n_h * d_h + rank * kv_w;
+    const int v_src0 = (n_h + n_kv) * d_h + rank * kv_w;
+    const int64_t chunks = h * ((q_w + 2 * kv_w) / 8);
+    int64_t blocks = (chunks + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(qkv_regroup_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W_qkv),
+                       static_cast<uint16_t*>(W_r), h, src_w, q_w, kv_w, q_src0, k_src0, v_src0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+tp_status tp_shard_shape(int32_t ndim, const int64_t* shape, int32_t elem_bytes, int32_t n_axes,
+                         const int64_t* axis_sizes, const uint32_t* dim_axis_mask, int64_t* local_shape_out,
+                         int64_t* local_bytes_out, int64_t* total_bytes_out) {
+    const char* fn = "tp_shard_shape";
+    if (ndim < 0 || ndim > 64) return fail(TP_ERR_INVALID_ARG, "%s: ndim = %d", fn, ndim);
+    if (n_axes < 0 || n_axes > 32) return fail(TP_ERR_INVALID_ARG, "%s: n_axes = %d", fn, n_axes);
+    if (elem_bytes <= 0) return fail(TP_ERR_INVALID_ARG, "%s: elem_bytes = %d", fn, elem_bytes);
+    if ((ndim > 0 && (!shape || !dim_axis_mask || !local_shape_out)) || (n_axes > 0 && !axis_sizes) ||
+        !local_bytes_out || !total_bytes_out)
+        return fail(TP_ERR_INVALID_ARG, "%s: NULL argument", fn);
+    int64_t devices = 1;
+    for (int a = 0; a < n_axes; ++a) {
+        if (axis_sizes[a] <= 0) return fail(TP_ERR_INVALID_ARG, "%s: mesh axis %d has size %lld", fn, a,
+                                            (long long)axis_sizes[a]);
+        devices *= axis_sizes[a];
+    }
+    uint32_t used = 0;
+    int64_t elems = 1;
+    for (int d = 0; d < ndim; ++d) {
+        const uint32_t m = dim_axis_mask[d];
+        if (n_axes < 32 && (m >> n_axes) != 0)
+            return fail(TP_ERR_INVALID_ARG, "%s: dim %d names a mesh axis >= %d", fn, d, n_axes);
+        if (m & used)
+            return fail(TP_ERR_INVALID_ARG, "%s: a mesh axis shards two dims (dim %d)", fn, d);
+        used |= m;
+        if (shape[d] < 0) return fail(TP_ERR_INVALID_ARG, "%s: dim %d is negative", fn, d);
+        int64_t div = 1;
+        for (int a = 0; a < n_axes; ++a)
+            if (m & (1u << a)) div *= axis_sizes[a];
+        if (shape[d] % div != 0)
+            return fail(TP_ERR_NOT_DIVISIBLE, "%s: dim %d (%lld) is not divisible by %lld", fn, d,
+                        (long long)shape[d], (long long)div);
+        local_shape_out[d] = shape[d] / div;
+        elems *= local_shape_out[d];
+    }
+    *local_bytes_out = elems * elem_bytes;
+    *total_bytes_out = elems * elem_bytes * devices;
+    return ok();
+}
+
+}  // extern "C"

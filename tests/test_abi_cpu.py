@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/tpshard.h declares, computes the host-only shard arithmetic, and
+rejects invalid arguments before any launch (null pointers never reach a
+kernel on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+import tensor_sharded_matmul_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(T.lib_path()),
+                                reason="libtpshard.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = T.load()
+    names = _declared()
+    assert {"tp_col_linear", "tp_row_linear_partial", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+            "tp_qkv_regroup", "tp_shard_shape"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version():
+    assert T.tp_version() >= 1
+
+
+def _mask(spec, axes):
+    return [sum(1 << axes.index(a) for a in dims) for dims in spec]
+
+
+def test_shard_shape_quiz_matches_oracle_and_page():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "shard_quiz.json")))
+    axes = [a for a, _ in g["mesh"]]
+    sizes = [s for _, s in g["mesh"]]
+    got = T.tp_shard_shape(g["shape"], g["elem_bytes"], sizes, _mask(g["spec"], axes))
+    assert list(got[0]) == g["local_shape"]
+    assert got[1] == g["local_bytes"] and got[2] == g["total_bytes"]
+    want = O.shard_shape(g["shape"], g["elem_bytes"], dict(g["mesh"]),
+                         [tuple(s) for s in g["spec"]])
+    assert got == want
+    with pytest.raises(ValueError, match="two dims"):
+        T.tp_shard_shape(g["shape"], 1, sizes, _mask(g["illegal_same_axis_spec"], axes))
+
+
+@pytest.mark.parametrize("shape,spec", [((8, 6), [("X",), ("Y",)]), ((8, 6), [("Y", "X"), ()]),
+                                        ((16, 4, 2), [(), ("X",), ("Y",)]), ((4,), [()]),
+                                        ((6, 6), [("X",), ()])])
+def test_shard_shape_agrees_with_oracle(shape, spec):
+    mesh = {"X": 4, "Y": 2}
+    axes = list(mesh)
+    try:
+        want = O.shard_shape(shape, 2, mesh, spec)
+    except O.ShardError:
+        with pytest.raises(ValueError):
+            T.tp_shard_shape(shape, 2, list(mesh.values()), _mask(spec, axes))
+        return
+    assert T.tp_shard_shape(shape, 2, list(mesh.values()), _mask(spec, axes)) == want
+
+
+def _raw(name):
+    return getattr(T.load(), name)
+
+
+NULL = ctypes.c_void_p(0)
+
+
+def test_regroup_divisibility_errors_before_launch():
+    f = _raw("tp_qkv_regroup")
+    assert f(NULL, NULL, 8192, 64, 8, 128, 7, 0, NULL) == 2          # NOT_DIVISIBLE
+    assert "must be a multiple of tensor_model_parallel_size" in T.tp_last_error()
+    assert f(NULL, NULL, 8192, 64, 8, 128, 16, 0, NULL) == 3         # n_kv < t: unsupported
+    assert f(NULL, NULL, 8192, 64, 8, 128, 8, 8, NULL) == 1          # rank out of range
+    assert f(NULL, NULL, 8192, 64, 8, 12, 8, 0, NULL) == 1           # d_h % 8
+    assert f(NULL, NULL, 8192, 64, 8, 128, 8, 0, NULL) == 1          # NULL pointers
+    assert "NULL" in T.tp_last_error()
+    assert f(NULL, NULL, 0, 64, 8, 128, 8, 0, NULL) == 0             # h = 0: nothing to do
+
+
+def test_gemm_entry_points_validate_before_launch():
+    col = _raw("tp_col_linear")
+    assert col(NULL, NULL, NULL, 16, 8192, 1280, 0, NULL, NULL) == 1          # NULL X
+    assert col(NULL, NULL, NULL, 16, 100, 1280, 0, NULL, NULL) == 3           # k % 64
+    assert col(NULL, NULL, NULL, -1, 8192, 1280, 0, NULL, NULL) == 1          # N < 0
+    assert col(NULL, NULL, NULL, 16, 8192, 1280, 7, NULL, NULL) == 1          # act
+    odd = ctypes.c_void_p(0x1008)
+    assert col(odd, odd, odd, 16, 8192, 1280, 0, NULL, NULL) == 1             # misaligned
+    assert "aligned" in T.tp_last_error()
+    row = _raw("tp_row_linear_partial")
+    assert row(NULL, NULL, NULL, 16, 1024, 8192, 0, NULL) == 1
+    fwd = _raw("tp_mlp_shard_fwd")
+    assert fwd(NULL, NULL, NULL, 16, 8192, 3584, 0, NULL, NULL, NULL, 0, NULL) == 1   # act NONE
+    bwd = _raw("tp_mlp_shard_bwd")
+    assert bwd(NULL, NULL, NULL, NULL, NULL, NULL, 16, 8192, 3584, 2, NULL, NULL, NULL, NULL, 0,
+               NULL) == 1
+    assert T.tp_last_error() != ""
