@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of a tensor-parallel layer on MI355X.
+
+Timed step: the Llama-3-70B (h=8192, F=28672) TP=8 SwiGLU MLP shard, forward
+(tp_mlp_shard_fwd: [gate|up] GEMM with the SiLU*up epilogue, then the
+row-parallel GEMM to the f32 partial) and backward (tp_mlp_shard_bwd: dY W_down^T
+with the SwiGLU backward epilogue, dX partial, dW_gate|up, dW_down), N = 4096
+tokens, bf16 inputs already resident in HBM. value = GEMM FLOPs of the step
+(2164.66 GFLOP) / time, in TFLOP/s.
+
+Also measured in the same run (reported under "rows"): every single-kernel
+GEMM of the step (HIP events on the stream the kernels run on), the fused-QKV
+regroup (GB/s, buffers rotated past the 256 MB Infinity Cache), the attention
+projections (QKV + W_O) forward and backward at N = 4096 and decode at N = 16,
+and the GPT-style GeLU MLP shard (N = 8192, h = 4096, F = 16384, t = 4). The
+fp64 oracle is timed on a bounded token sample of the same MLP workload on the
+host cores (cpu_baseline).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0         # HBM3E
+METRIC = "TFLOP/s + % bf16 MFMA peak, Llama-3-70B TP=8 MLP shard fwd+bwd, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=10, help="repetitions per single-kernel timing")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="token sample for the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the TP layer; --gpus {args.gpus} is not "
+              "supported (this build runs on a single GPU and has no collectives).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import synth
+    import tensor_sharded_matmul_amd as T
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    T.load()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- workload: Llama-3-70B SwiGLU MLP shard, t = 8 ----------------
+    w = synth.WORKLOADS["llama70b_swiglu_t8"]
+    wb = synth.WORKLOADS["llama70b_swiglu_t8_bwd"]
+    N, h, f = w.N, w.h, w.f
+    t0 = time.perf_counter()
+    d = synth.mlp_inputs(w.seed, N, h, w.F, w.t, "swiglu")
+    dY_bits = synth.mlp_bwd_inputs(wb.seed, N, h)["dY"]
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+    X, W_in, W_out, dY = to_dev(d["X"]), to_dev(d["W_in"]), to_dev(d["W_out"]), to_dev(dY_bits)
+    bf, f32 = torch.bfloat16, torch.float32
+    Z = torch.empty((N, f), dtype=bf, device=dev)
+    H = torch.empty((N, 2 * f), dtype=bf, device=dev)
+    P = torch.empty((N, h), dtype=f32, device=dev)
+    dH = torch.empty((N, 2 * f), dtype=bf, device=dev)
+    dX = torch.empty((N, h), dtype=f32, device=dev)
+    dWi = torch.empty((h, 2 * f), dtype=f32, device=dev)
+    dWo = torch.empty((f, h), dtype=f32, device=dev)
+
+    fl = {
+        "gemm1_gate_up_swiglu": 2 * N * (2 * f) * h,
+        "gemm2_down_partial": 2 * N * h * f,
+        "bwd_dz_swiglu": 2 * N * f * h,
+        "bwd_dx_partial": 2 * N * h * (2 * f),
+        "bwd_dw_gate_up": 2 * h * (2 * f) * N,
+        "bwd_dw_down": 2 * f * h * N,
+    }
+    fwd_flops = fl["gemm1_gate_up_swiglu"] + fl["gemm2_down_partial"]
+    bwd_flops = sum(v for k, v in fl.items() if k.startswith("bwd"))
+    step_flops = fwd_flops + bwd_flops
+
+    def fwd():
+        T.tp_mlp_shard_fwd(X, W_in, W_out, "swiglu", Z=Z, H_save=H, P=P)
+
+    def bwd():
+        T.tp_mlp_shard_bwd(X, W_in, W_out, H, Z, dY, "swiglu", dH=dH, dX_part=dX, dW_in=dWi,
+                           dW_out=dWo)
+
+    def step():
+        fwd()
+        bwd()
+
+    stream = torch.cuda.current_stream()
+
+    def time_fn(fn, reps, warm=2):
+        """Average ms per call: one HIP event pair per call on the launch stream."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        return float(np.mean(ts)), float(np.median(ts)), float(np.min(ts))
+
+    # ---------------- timed region: K steps ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] step {ms_step:.4f} ms  {value:.1f} TFLOP/s  "
+        f"{100 * value / PEAK_BF16_TFLOPS:.1f}% of peak  (wall {wall:.3f}s)")
+
+    # ---------------- per-kernel timings (single-kernel entry points) ----------------
+    kern = {
+        "gemm1_gate_up_swiglu": (lambda: T.tp_col_linear(X, W_in, "swiglu", Y=Z, H_save=H),
+                                 "gemm_kernel<256, 256, false, true, 3>"),
+        "gemm2_down_partial": (lambda: T.tp_row_linear_partial(Z, W_out, P=P),
+                               "gemm_kernel<256, 256, false, true, 0>"),
+        "bwd_dx_partial": (lambda: T.tp_col_linear_bwd(X, W_in, dH, dX_part=dX, want_dw=False),
+                           "gemm_kernel<256, 256, false, false, 0>"),
+        "bwd_dw_gate_up": (lambda: T.tp_col_linear_bwd(X, W_in, dH, dW=dWi, want_dx=False),
+                           "gemm_kernel<256, 256, true, true, 0>"),
+        "bwd_dw_down": (lambda: T.tp_row_linear_bwd(Z, W_out, dY, dW=dWo, want_dz=False),
+                        "gemm_kernel<256, 256, true, true, 0>"),
+    }
+    kt = {}
+    for name, (fn, kname) in kern.items():
+        mean, med, mn = time_fn(fn, args.reps)
+        kt[name] = {"kernel": kname, "ms": round(mean, 4), "ms_median": round(med, 4),
+                    "tflops": round(fl[name] / (mean * 1e-3) / 1e12, 1)}
+        log(f"[bench] {name:24s} {mean:.4f} ms  {kt[name]['tflops']} TFLOP/s")
+    bwd_mean = time_fn(bwd, args.reps)[0]
+    dz_ms = bwd_mean - sum(kt[k]["ms"] for k in ("bwd_dx_partial", "bwd_dw_gate_up", "bwd_dw_down"))
+    kt["bwd_dz_swiglu"] = {"kernel": "gemm_kernel<256, 256, false, false, 5>",
+                           "ms": round(dz_ms, 4), "derived": "bwd total minus the other three",
+                           "tflops": round(fl["bwd_dz_swiglu"] / (dz_ms * 1e-3) / 1e12, 1)}
+
+    # dominant kernel: the largest share of the step; per-launch average of that kernel
+    by_kernel = {}
+    for name, r in kt.items():
+        e = by_kernel.setdefault(r["kernel"], {"ms": 0.0, "flops": 0, "launches": 0})
+        e["ms"] += r["ms"]
+        e["flops"] += fl[name]
+        e["launches"] += 1
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
+    per_launch_flops = dom["flops"] / dom["launches"]
+    per_launch_ms = dom["ms"] / dom["launches"]
+    achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": per_launch_flops, "avg_launch_ms": round(per_launch_ms, 4)}
+
+    rows = {"mlp_kernels": kt,
+            "fwd_ms": round(time_fn(fwd, args.reps)[0], 4), "bwd_ms": round(bwd_mean, 4)}
+    rows["fwd_tflops"] = round(fwd_flops / (rows["fwd_ms"] * 1e-3) / 1e12, 1)
+    rows["bwd_tflops"] = round(bwd_flops / (rows["bwd_ms"] * 1e-3) / 1e12, 1)
+
+    del Z, H, P, dH, dX, dWi, dWo
+    if not args.no_rows:
+        rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, args.reps))
+    torch.cuda.synchronize()
+
+    # ---------------- CPU baseline: the oracle on a token sample ----------------
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(d, dY_bits, args.cpu_tokens, synth, np)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": "llama3-70b-tp8-swiglu-mlp-shard-fwd-bwd", "tokens": N, "h": h,
+                   "F": w.F, "t": w.t, "f": f, "step_gflop": round(step_flops / 1e9, 2)},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "device": {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, reps):
+    """The other rows of the hot path, each timed on its own."""
+    res = {}
+    bf, f32 = torch.bfloat16, torch.float32
+    # --- fused-QKV regroup, Llama-3-70B t=8, 4 rotated source copies (> Infinity Cache) ---
+    q = synth.WORKLOADS["llama70b_qkv_t8"]
+    n_h, n_kv, d_h, t, h = q.n_h, q.n_kv, q.d_h, q.t, q.h
+    width = (n_h + 2 * n_kv) * d_h
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(q.seed)
+    srcs = [torch.randn((h, width), device=dev, dtype=f32, generator=gen).to(bf) for _ in range(4)]
+    dsts = [torch.empty((h, width // t), device=dev, dtype=bf) for _ in range(4)]
+    it = [0]
+
+    def regroup():
+        i = it[0]
+        it[0] += 1
+        T.tp_qkv_regroup(srcs[i % 4], n_h, n_kv, d_h, t, (i // 4) % t, W_r=dsts[i % 4])
+
+    ms = time_fn(regroup, max(reps, 32), warm=4)[0]
+    moved = 2 * h * (width // t) * 2
+    res["qkv_regroup"] = {"ms": round(ms, 5), "bytes": moved,
+                          "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    del srcs, dsts
+
+    # --- attention projections: QKV column GEMM + W_O row partial, fwd and bwd ---
+    dq = synth.qkv_inputs(q.seed, q.N, h, n_h, n_kv, d_h, t)
+    Wr_bits = dq["W_qkv"][:, :width // t]   # rank-0 shape; values do not change timing
+    W_r, W_O = to_dev(np.ascontiguousarray(Wr_bits)), to_dev(dq["W_O"])
+    X, O, dQKV, dY = to_dev(dq["X"]), to_dev(dq["O"]), to_dev(dq["dQKV"]), to_dev(dq["dY"])
+    Nq = q.N
+    Y = torch.empty((Nq, width // t), dtype=bf, device=dev)
+    P = torch.empty((Nq, h), dtype=f32, device=dev)
+    fl_fwd = 2 * Nq * h * (width // t) + 2 * Nq * (n_h * d_h // t) * h
+
+    def attn_fwd():
+        T.tp_col_linear(X, W_r, "none", Y=Y)
+        T.tp_row_linear_partial(O, W_O, P=P)
+
+    ms = time_fn(attn_fwd, reps)[0]
+    res["attn_proj_fwd_prefill"] = {"ms": round(ms, 4), "gflop": round(fl_fwd / 1e9, 2),
+                                    "tflops": round(fl_fwd / (ms * 1e-3) / 1e12, 1)}
+    dXq = torch.empty((Nq, h), dtype=f32, device=dev)
+    dWq = torch.empty((h, width // t), dtype=f32, device=dev)
+    dO = torch.empty((Nq, n_h * d_h // t), dtype=bf, device=dev)
+    dWO = torch.empty((n_h * d_h // t, h), dtype=f32, device=dev)
+
+    def attn_bwd():
+        T.tp_col_linear_bwd(X, W_r, dQKV, dX_part=dXq, dW=dWq)
+        T.tp_row_linear_bwd(O, W_O, dY, dZ=dO, dW=dWO)
+
+    ms = time_fn(attn_bwd, reps)[0]
+    res["attn_proj_bwd_prefill"] = {"ms": round(ms, 4), "gflop": round(2 * fl_fwd / 1e9, 2),
+                                    "tflops": round(2 * fl_fwd / (ms * 1e-3) / 1e12, 1)}
+    del dXq, dWq, dO, dWO, Y, P
+    # decode, N = 16: weights rotated over 16 copies (> Infinity Cache)
+    Wrs = [W_r.clone() for _ in range(16)]
+    WOs = [W_O.clone() for _ in range(16)]
+    Xd, Od = X[:16].contiguous(), O[:16].contiguous()
+    Yd = torch.empty((16, width // t), dtype=bf, device=dev)
+    Pd = torch.empty((16, h), dtype=f32, device=dev)
+    it[0] = 0
+
+    def decode():
+        i = it[0] % 16
+        it[0] += 1
+        T.tp_col_linear(Xd, Wrs[i], "none", Y=Yd)
+        T.tp_row_linear_partial(Od, WOs[i], P=Pd)
+
+    ms = time_fn(decode, max(reps, 32), warm=4)[0]
+    wbytes = 2 * h * (width // t) + 2 * (n_h * d_h // t) * h
+    res["attn_proj_decode_n16"] = {"ms": round(ms, 4), "weight_bytes": wbytes,
+                                   "gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    del Wrs, WOs, X, O, dQKV, dY, W_r, W_O
+
+    # --- GPT-style GeLU MLP shard, t = 4, forward ---
+    g = synth.WORKLOADS["gpt_gelu_t4"]
+    dg = synth.mlp_inputs(g.seed, g.N, g.h, g.F, g.t, "gelu")
+    Xg, Ag, Bg = to_dev(dg["X"]), to_dev(dg["W_in"]), to_dev(dg["W_out"])
+    Zg = torch.empty((g.N, g.f), dtype=bf, device=dev)
+    Hg = torch.empty((g.N, g.f), dtype=bf, device=dev)
+    Pg = torch.empty((g.N, g.h), dtype=f32, device=dev)
+    flg = 2 * 2 * g.N * g.h * g.f
+    ms = time_fn(lambda: T.tp_mlp_shard_fwd(Xg, Ag, Bg, "gelu", Z=Zg, H_save=Hg, P=Pg), reps)[0]
+    res["gpt_gelu_mlp_fwd_t4"] = {"ms": round(ms, 4), "gflop": round(flg / 1e9, 2),
+                                  "tflops": round(flg / (ms * 1e-3) / 1e12, 1)}
+    return res
+
+
+def cpu_baseline(d, dY_bits, n_tok, synth, np):
+    """The fp64 oracle as it stands, on the first n_tok tokens of the same MLP workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()
+                       if i.get("internal_api") == "openblas"), default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    X = synth.bf16_to_f64(d["X"][:n_tok])
+    W_in = synth.bf16_to_f64(d["W_in"])
+    W_out = synth.bf16_to_f64(d["W_out"])
+    dY = synth.bf16_to_f64(dY_bits[:n_tok])
+    h, n_w = W_in.shape
+    f = W_out.shape[0]
+    t0 = time.perf_counter()
+    O.mlp_shard_fwd(X, W_in, W_out, "swiglu")
+    O.mlp_shard_bwd(X, W_in, W_out, dY, "swiglu")
+    dt = time.perf_counter() - t0
+    flops = 3 * (2 * n_tok * n_w * h + 2 * n_tok * h * f)
+    log(f"[bench] oracle fp64 on {n_tok} tokens: {dt:.2f}s, {flops / dt / 1e9:.1f} GFLOP/s, "
+        f"{threads} threads")
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"MLP shard fwd+bwd on the first {n_tok} of 4096 tokens (fp64 numpy/OpenBLAS); "
+                      f"{dt:.2f} s for {flops / 1e9:.1f} GFLOP"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -7,22 +7,31 @@
 //   NT  A[M][K], B[N][K]   input gradients  (dY W^T)
 //   TN  A[K][M], B[K][N]   weight gradients (X^T dY)
 // and fuses the shard's elementwise work into the epilogue
-// ([TPSP] "MLP：先列后行": GeLU / SiLU(gate)*up are local, per element).
+// ([TPSP] "MLP：先列后行": GeLU and SiLU(gate)*up are local, per element).
 //
 // Design (gfx950 / CDNA4):
-//  * 256 threads = 4 waves of 64 in a 2x2 grid; each wave owns a
-//    (BM/2) x (BN/2) sub-tile of C held in f32 accumulators
-//    (128 x 128 -> 256 accumulator registers per lane).
-//  * v_mfma_f32_16x16x32_bf16, with operands swapped (the MFMA "A" operand is
-//    the B tile) so that each lane ends with 4 *consecutive columns* of one C
-//    row: epilogue stores are 16-byte (f32) or 8-byte (bf16) vectors.
-//  * LDS holds both tiles K-contiguous ([row][k], 64 k per stage, rows padded
-//    to 72 elements = 144 B so that the 16 rows read by one MFMA fragment load
-//    fall in distinct banks). Two stages (double buffer), one barrier per
-//    K step; the next stage's global loads are in flight during the MFMAs.
-//  * Operands stored MN-contiguous in HBM (B in NN, both in TN) are loaded as
-//    8x8 bf16 blocks and transposed in registers with byte permutes before
-//    the 16-byte LDS writes, so the MFMA loop is the same for every layout.
+//  * WAVES_M x WAVES_N waves of 64 lanes; each wave owns a (BM/WAVES_M) x
+//    (BN/WAVES_N) sub-tile of C in f32 accumulators.
+//  * v_mfma_f32_16x16x32_bf16 with the operands swapped (the MFMA "A" operand
+//    is the B tile), so each lane ends with 4 consecutive columns of one C row
+//    and epilogue stores are 16-byte (f32) or 8-byte (bf16) vectors.
+//  * Operand tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
+//    staging registers), STAGES deep, so STAGES-1 K-steps of loads are in
+//    flight while the MFMAs consume the oldest one; one barrier per K-step.
+//    The loads are issued from inline asm with explicit vmcnt waits, because
+//    the compiler would otherwise drain every LDS-DMA load before each
+//    barrier. Rows past K (and past M / N) read as zero through the buffer
+//    descriptor's range check.
+//  * LDS layouts keep the operand as stored in HBM:
+//      K-contiguous tile [rows][BK]: 16-byte chunk c of row r is stored at
+//        c ^ swz(r), swz(r) = (r>>1)&7 (BK=64) or (r>>2)&3 (BK=32), so the 16
+//        rows one MFMA fragment read touches fall in 16 distinct bank groups
+//        (gfx950 LDS: 64 banks x 4 B, 16 lanes of a ds_read_b128 per clock).
+//      MN-contiguous tile [BK][cols]: chunk c of k-row k at c ^ (2(k&3) +
+//        8((k>>3)&1)); fragments are read with ds_read_b64_tr_b16, which
+//        transposes 4x4 blocks of 16-bit values across each 16-lane group,
+//        giving every lane 4 consecutive k of one column.
+//    so the MFMA inner loop is the same for every layout.
 //  * Workgroup -> tile mapping is XCD-aware: the hardware deals workgroups
 //    round-robin over the 8 XCDs, so consecutive blocks of tiles are mapped
 //    to one XCD (sharing its L2), grouped GROUP_M tile rows at a time.
@@ -31,16 +40,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tps {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;        // K per pipeline stage
-constexpr int kLdsStride = 72; // bf16 elements per LDS row (64 + 8 pad)
 constexpr int kGroupM = 4;     // tile rows per L2 group
 
 enum Epi : int {
@@ -63,6 +73,7 @@ struct GemmArgs {
     int ldc, ldc2;   // leading dims of C and C2 / aux (elements)
     int f;           // SWIGLU / SWIGLU_BWD: column offset of the "up" half
     int accumulate;  // EPI_F32: add into C
+    uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (buffer range check)
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
@@ -95,99 +106,62 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register loaders. Each returns the 16-byte chunks a thread owns;
-// the matching LDS writer puts them in the [row][k] tile.
+// Buffer descriptor and the LDS-DMA load (16 bytes per lane; lane l writes
+// LDS bytes [m0 + 16 l, m0 + 16 l + 16)).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r[0] = (int32_t)(uint32_t)p;
+    r[1] = (int32_t)((uint32_t)(p >> 32) & 0xffffu);  // stride 0, no swizzle
+    r[2] = (int32_t)bytes;                            // range-checked extent
+    r[3] = 0x00020000;                                // gfx9 data format word
+    return r;
+}
 
-// K-contiguous operand: rows x 64 k. Chunk q = tid + 256 i: row q/8, k-chunk q%8.
-template <int ROWS>
-struct KContigLoader {
-    static constexpr int kLoads = ROWS * 8 / kThreads;
-    static_assert(ROWS * 8 % kThreads == 0, "tile rows must be a multiple of 32");
-    u32x4_t r[kLoads];
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+}
 
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int ld,
-                                         int row0, int rows_total, int k0, int tid) {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int q = tid + kThreads * i;
-            const int row = row0 + (q >> 3);
-            const int kc = k0 + (q & 7) * 8;
-            if (row < rows_total) {
-                r[i] = *reinterpret_cast<const u32x4_t*>(base + (size_t)row * ld + kc);
-            } else {
-                r[i] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    }
+// Wait until at most N of this wave's LDS-DMA loads are outstanding and its LDS
+// reads are done, then barrier: afterwards every wave's loads of the stage the
+// wait covers are in LDS, and no wave still reads the stage about to be refilled.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            const int q = tid + kThreads * i;
-            *reinterpret_cast<u32x4_t*>(lds + (q >> 3) * kLdsStride + (q & 7) * 8) = r[i];
-        }
-    }
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-// MN-contiguous operand stored [K][cols]: 64 k x ROWS columns, loaded as 8x8
-// blocks (block b: k-chunk b%8, column group b/8) and transposed in registers.
-// COLMAP maps a tile column group to a global column (or -1 = zero fill).
-template <int ROWS>
-struct MNContigLoader {
-    static constexpr int kBlocks = ROWS;  // 8 k-chunks x ROWS/8 column groups
-    static constexpr int kPerThread = (kBlocks + kThreads - 1) / kThreads;
-    u32x4_t r[kPerThread][8];
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)addr);
+}
 
-    template <class ColMap>
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int ld,
-                                         int k0, int k_total, int tid, const ColMap& colmap) {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int b = tid + kThreads * p;
-            const int kb = b & 7;
-            const int cg = b >> 3;
-            const int gcol = (b < kBlocks) ? colmap(cg * 8) : -1;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int gk = k0 + kb * 8 + kk;
-                if (gcol >= 0 && gk < k_total) {
-                    r[p][kk] = *reinterpret_cast<const u32x4_t*>(base + (size_t)gk * ld + gcol);
-                } else {
-                    r[p][kk] = u32x4_t{0u, 0u, 0u, 0u};
-                }
-            }
-        }
-    }
+__device__ __forceinline__ bf16x8_t lds_read_tr2(uint32_t addr0, uint32_t addr1) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr0);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
-    __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-        for (int p = 0; p < kPerThread; ++p) {
-            const int b = tid + kThreads * p;
-            if (b >= kBlocks) continue;
-            const int kb = b & 7;
-            const int cg = b >> 3;
-            // r[p][kk] word w holds columns (2w, 2w+1) of row k = kb*8 + kk.
-            // out[e] word w must hold rows (2w, 2w+1) of column e.
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                u32x4_t o;
-                o[0] = __builtin_amdgcn_perm(r[p][1][e >> 1], r[p][0][e >> 1], sel);
-                o[1] = __builtin_amdgcn_perm(r[p][3][e >> 1], r[p][2][e >> 1], sel);
-                o[2] = __builtin_amdgcn_perm(r[p][5][e >> 1], r[p][4][e >> 1], sel);
-                o[3] = __builtin_amdgcn_perm(r[p][7][e >> 1], r[p][6][e >> 1], sel);
-                *reinterpret_cast<u32x4_t*>(lds + (cg * 8 + e) * kLdsStride + kb * 8) = o;
-            }
-        }
-    }
-};
+// swizzles (see the header comment)
+template <int BK>
+__device__ __forceinline__ int swz_k(int row) {
+    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+__device__ __forceinline__ int swz_mn(int k) {
+    return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+}
 
 struct IdentityCols {
     int col0, cols_total;
     __device__ __forceinline__ int operator()(int c) const {
         const int g = col0 + c;
-        return g < cols_total ? g : -1;
+        return g < cols_total ? g : 0;  // columns past the edge: any valid column
     }
 };
 
@@ -200,121 +174,101 @@ struct SwigluCols {
         const int wc = c / WN;
         const int p = c % WN;
         const int j = z0 + wc * (WN / 2) + (p % (WN / 2));
-        if (j >= f) return -1;
+        if (j >= f) return 0;  // outputs past f are never stored
         return p < WN / 2 ? j : f + j;
     }
 };
 
 // ---------------------------------------------------------------------------
-// The kernel.
+// Per-lane DMA offsets of one operand tile (bytes, relative to the matrix).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool A_T, bool B_KN, int EPI>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_kernel(const GemmArgs args) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int MI = WM / 16, NI = WN / 16;
-    constexpr bool SWIGLU = (EPI == EPI_SWIGLU);
-    constexpr int BNZ = SWIGLU ? BN / 2 : BN;  // output columns per tile
-    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert(!SWIGLU || (NI % 2 == 0 && B_KN), "SwiGLU needs an even gate/up split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * kLdsStride];
+// K-contiguous operand [rows][K]: tile [R][BK].
+template <int R, int BK, int NWAVES>
+struct KTileDma {
+    static constexpr int kCpr = BK / 8;              // 16-byte chunks per row
+    static constexpr int kRpi = 64 / kCpr;           // rows per 1 KB instruction
+    static constexpr int kInst = R * kCpr / 64;      // instructions per tile
+    static constexpr int kPerWave = kInst / NWAVES;
+    static_assert(kInst % NWAVES == 0, "tile rows must split evenly over the waves");
+    uint32_t off[kPerWave];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 15, lq = lane >> 4;
-
-    // --- tile index (XCD-aware, grouped) ---
-    const int tiles_m = (args.M + BM - 1) / BM;
-    const int tiles_n = (args.N + BNZ - 1) / BNZ;
-    const int T = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int per = T >> 3;
-    const int lid = (bid < per * 8) ? (bid & 7) * per + (bid >> 3) : bid;
-    const int group = lid / (kGroupM * tiles_n);
-    const int first_m = group * kGroupM;
-    const int gsz = min(tiles_m - first_m, kGroupM);
-    const int in_group = lid % (kGroupM * tiles_n);
-    const int tm = first_m + in_group % gsz;
-    const int tn = in_group / gsz;
-    const int m0 = tm * BM;
-    const int n0 = tn * BNZ;
-
-    using ALoader = typename std::conditional<A_T, MNContigLoader<BM>, KContigLoader<BM>>::type;
-    using BLoader = typename std::conditional<B_KN, MNContigLoader<BN>, KContigLoader<BN>>::type;
-    ALoader la;
-    BLoader lb;
-
-    const int KT = (args.K + kBK - 1) / kBK;
-
-    auto load_stage = [&](int kt) {
-        const int k0 = kt * kBK;
-        if constexpr (A_T) {
-            la.load(args.A, args.lda, k0, args.K, tid, IdentityCols{m0, args.M});
-        } else {
-            la.load(args.A, args.lda, m0, args.M, k0, tid);
-        }
-        if constexpr (B_KN) {
-            if constexpr (SWIGLU) {
-                lb.load(args.B, args.ldb, k0, args.K, tid, SwigluCols<WN>{n0, args.f});
-            } else {
-                lb.load(args.B, args.ldb, k0, args.K, tid, IdentityCols{n0, args.N});
-            }
-        } else {
-            lb.load(args.B, args.ldb, n0, args.N, k0, tid);
-        }
-    };
-    auto store_stage = [&](int buf) {
-        uint16_t* As = smem + buf * (BM + BN) * kLdsStride;
-        uint16_t* Bs = As + BM * kLdsStride;
-        la.store(As, tid);
-        lb.store(Bs, tid);
-    };
-
-    f32x4_t acc[MI][NI];
+    __device__ __forceinline__ void init(int wave, int lane, int row0, int ld) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    if (KT > 0) {
-        load_stage(0);
-        store_stage(0);
+        for (int i = 0; i < kPerWave; ++i) {
+            const int I = wave * kPerWave + i;
+            const int row = I * kRpi + lane / kCpr;
+            const int c = (lane % kCpr) ^ swz_k<BK>(row);
+            off[i] = (uint32_t)(row0 + row) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
+        }
     }
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_stage(kt + 1);
-
-        const uint16_t* As = smem + cur * (BM + BN) * kLdsStride + (wm * WM + lr) * kLdsStride;
-        const uint16_t* Bs = smem + cur * (BM + BN) * kLdsStride + (BM + wn * WN + lr) * kLdsStride;
+    __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t lds_tile, int wave, uint32_t kbytes) const {
 #pragma unroll
-        for (int s = 0; s < kBK / 32; ++s) {
-            bf16x8_t af[MI], bfr[NI];
-            const int koff = s * 32 + lq * 8;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 16 * kLdsStride + koff);
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 16 * kLdsStride + koff);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j],
-                                                                         0, 0, 0);
-        }
-
-        if (kt + 1 < KT) store_stage(cur ^ 1);
-        __syncthreads();
+        for (int i = 0; i < kPerWave; ++i)
+            dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
     }
+    static constexpr uint32_t step_bytes(int /*ld*/) { return BK * 2; }
+};
 
-    // --- epilogue: lane holds C[m][n .. n+3] for each (i, j) block ---
+// MN-contiguous operand [K][cols]: tile [BK][C].
+template <int C, int BK, int NWAVES>
+struct MNTileDma {
+    static constexpr int kCpr = C / 8;
+    static constexpr int kRpi = 64 / kCpr;
+    static constexpr int kInst = BK * kCpr / 64;
+    static constexpr int kPerWave = kInst / NWAVES;
+    static_assert(kCpr >= 16 && 64 % kCpr == 0, "MN tile needs 128..512 columns");
+    static_assert(kInst % NWAVES == 0, "tile must split evenly over the waves");
+    uint32_t off[kPerWave];
+
+    template <class ColMap>
+    __device__ __forceinline__ void init(int wave, int lane, int ld, const ColMap& colmap) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const int I = wave * kPerWave + i;
+            const int k = I * kRpi + lane / kCpr;
+            const int c = (lane % kCpr) ^ swz_mn(k);
+            off[i] = (uint32_t)k * (uint32_t)ld * 2u + (uint32_t)colmap(c * 8) * 2u;
+        }
+    }
+    __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t lds_tile, int wave, uint32_t kbytes) const {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i)
+            dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
+    }
+};
+
+// Fragment address of one 16x32 MFMA operand block (rows rb..rb+15, k32 step s).
+template <int BK>
+__device__ __forceinline__ uint32_t ktile_frag_addr(uint32_t tile, int rb, int s, int lane) {
+    const int x = lane & 15, g = lane >> 4;
+    const int row = rb + x;
+    const int c = (4 * s + g) ^ swz_k<BK>(row);
+    return tile + (uint32_t)(row * BK * 2 + c * 16);
+}
+
+// The two ds_read_b64_tr_b16 addresses of a 16x32 operand block whose index
+// (column of the [BK][C] tile) runs over cb..cb+15, k32 step s.
+template <int C>
+__device__ __forceinline__ void mntile_frag_addr(uint32_t tile, int cb, int s, int lane, uint32_t& a0,
+                                                 uint32_t& a1) {
+    const int x = lane & 15, g = lane >> 4;
+    const int col = cb + 4 * (x & 3);
+    const int k0 = 32 * s + 8 * g + (x >> 2);
+    const int k1 = k0 + 4;
+    const int c0 = (col >> 3) ^ swz_mn(k0);
+    const int c1 = (col >> 3) ^ swz_mn(k1);
+    const int h = (col & 7) * 2;  // 0 or 8 bytes inside the chunk
+    a0 = tile + (uint32_t)(k0 * C * 2 + c0 * 16 + h);
+    a1 = tile + (uint32_t)(k1 * C * 2 + c1 * 16 + h);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue: lane holds C[m][n .. n+3] of each 16x16 block (i, j).
+// ---------------------------------------------------------------------------
+template <int MI, int NI, int WM, int WN, int EPI>
+__device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int m0,
+                                         int n0, int wm, int wn, int lr, int lq) {
     const int mb = m0 + wm * WM + lr;
     if constexpr (EPI == EPI_F32) {
         float* C = reinterpret_cast<float*>(args.C);
@@ -437,6 +391,149 @@ gemm_kernel(const GemmArgs args) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_T, bool B_KN, int EPI>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+gemm_kernel(const GemmArgs args) {
+    constexpr int NWAVES = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int MI = WM / 16, NI = WN / 16;
+    constexpr bool SWIGLU = (EPI == EPI_SWIGLU);
+    constexpr int BNZ = SWIGLU ? BN / 2 : BN;  // output columns per tile
+    constexpr int STAGE_BYTES = (BM + BN) * BK * 2;
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(!SWIGLU || (NI % 2 == 0 && B_KN), "SwiGLU needs an even gate/up split");
+    static_assert(STAGES >= 2, "at least two stages");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // --- tile index (XCD-aware, grouped) ---
+    const int tiles_m = (args.M + BM - 1) / BM;
+    const int tiles_n = (args.N + BNZ - 1) / BNZ;
+    const int T = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int per = T >> 3;
+    const int lid = (bid < per * 8) ? (bid & 7) * per + (bid >> 3) : bid;
+    const int group = lid / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsz = min(tiles_m - first_m, kGroupM);
+    const int in_group = lid % (kGroupM * tiles_n);
+    const int tm = first_m + in_group % gsz;
+    const int tn = in_group / gsz;
+    const int m0 = tm * BM;
+    const int n0 = tn * BNZ;
+
+    // --- DMA descriptors and per-lane offsets ---
+    const i32x4_t rsA = make_rsrc(args.A, args.a_bytes);
+    const i32x4_t rsB = make_rsrc(args.B, args.b_bytes);
+    using ADma = typename std::conditional<A_T, MNTileDma<BM, BK, NWAVES>, KTileDma<BM, BK, NWAVES>>::type;
+    using BDma = typename std::conditional<B_KN, MNTileDma<BN, BK, NWAVES>, KTileDma<BN, BK, NWAVES>>::type;
+    ADma da;
+    BDma db;
+    if constexpr (A_T) {
+        da.init(wave, lane, args.lda, IdentityCols{m0, args.M});
+    } else {
+        da.init(wave, lane, m0, args.lda);
+    }
+    if constexpr (B_KN) {
+        if constexpr (SWIGLU) {
+            db.init(wave, lane, args.ldb, SwigluCols<WN>{n0, args.f});
+        } else {
+            db.init(wave, lane, args.ldb, IdentityCols{n0, args.N});
+        }
+    } else {
+        db.init(wave, lane, n0, args.ldb);
+    }
+    const uint32_t a_step = A_T ? (uint32_t)BK * (uint32_t)args.lda * 2u : (uint32_t)BK * 2u;
+    const uint32_t b_step = B_KN ? (uint32_t)BK * (uint32_t)args.ldb * 2u : (uint32_t)BK * 2u;
+    const uint32_t lds0 = lds_addr(smem);
+    constexpr int LOADS_PER_STAGE = ADma::kPerWave + BDma::kPerWave;
+
+    auto issue = [&](int kt) {
+        const uint32_t st = lds0 + (uint32_t)((kt % STAGES) * STAGE_BYTES);
+        da.issue(rsA, st, wave, (uint32_t)kt * a_step);
+        db.issue(rsB, st + BM * BK * 2, wave, (uint32_t)kt * b_step);
+    };
+
+    // --- fragment base addresses (stage 0) ---
+    uint32_t fa[MI][BK / 32][2];
+    uint32_t fb[NI][BK / 32][2];
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            if constexpr (A_T) {
+                mntile_frag_addr<BM>(lds0, wm * WM + 16 * i, s, lane, fa[i][s][0], fa[i][s][1]);
+            } else {
+                fa[i][s][0] = ktile_frag_addr<BK>(lds0, wm * WM + 16 * i, s, lane);
+                fa[i][s][1] = 0;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            if constexpr (B_KN) {
+                mntile_frag_addr<BN>(lds0 + BM * BK * 2, wn * WN + 16 * j, s, lane, fb[j][s][0], fb[j][s][1]);
+            } else {
+                fb[j][s][0] = ktile_frag_addr<BK>(lds0 + BM * BK * 2, wn * WN + 16 * j, s, lane);
+                fb[j][s][1] = 0;
+            }
+        }
+    }
+
+    f32x4_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (args.K + BK - 1) / BK;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < KT) issue(st);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + STAGES - 2 < KT) {
+            wait_vmcnt_barrier<(STAGES - 2) * LOADS_PER_STAGE>();
+        } else {
+            wait_vmcnt_barrier<0>();
+        }
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+
+        const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            bf16x8_t af[MI], bfr[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                if constexpr (A_T) af[i] = lds_read_tr2(fa[i][s][0] + so, fa[i][s][1] + so);
+                else af[i] = lds_read16(fa[i][s][0] + so);
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                if constexpr (B_KN) bfr[j] = lds_read_tr2(fb[j][s][0] + so, fb[j][s][1] + so);
+                else bfr[j] = lds_read16(fb[j][s][0] + so);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    epilogue<MI, NI, WM, WN, EPI>(acc, args, m0, n0, wm, wn, lr, lq);
 }
 
 }  // namespace tps

@@ -86,25 +86,38 @@ static tp_status check_elems(const char* fn, int64_t rows, int64_t cols) {
 // ---------------------------------------------------------------------------
 enum Layout { NN, NT, TN };
 
-template <int BM, int BN, bool A_T, bool B_KN, int EPI>
+template <int BM, int BN, int BK, int ST, int WVM, int WVN, bool A_T, bool B_KN, int EPI>
 static tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
     constexpr int BNZ = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + BNZ - 1) / BNZ);
     if (tiles == 0) return TP_OK;
     if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, A_T, B_KN, EPI>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, ST, WVM, WVN, A_T, B_KN, EPI>), dim3((unsigned)tiles),
+                       dim3(64 * WVM * WVN), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return TP_OK;
 }
 
+// Operands are addressed with 32-bit byte offsets (buffer descriptors).
+static constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
+
 template <bool A_T, bool B_KN, int EPI>
-static tp_status launch_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
+static tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
     if (a.M == 0 || a.N == 0) return TP_OK;
+    const int64_t a_bytes = (int64_t)(A_T ? a.K : a.M) * a.lda * 2;
+    const int64_t b_bytes = (int64_t)(B_KN ? a.K : a.N) * a.ldb * 2;
+    if (a_bytes > kMaxOperandBytes || b_bytes > kMaxOperandBytes)
+        return fail(TP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+    a.a_bytes = (uint32_t)a_bytes;
+    a.b_bytes = (uint32_t)b_bytes;
     // Large problems: 256x256 tiles (128x128 per wave). Few rows: 64x128.
-    if (a.M >= 256 || A_T) return launch_cfg<256, 256, A_T, B_KN, EPI>(fn, a, s);
-    return launch_cfg<64, 128, A_T, B_KN, EPI>(fn, a, s);
+    if constexpr (A_T) {
+        return launch_cfg<256, 256, 32, 4, 2, 2, A_T, B_KN, EPI>(fn, a, s);
+    } else {
+        if (a.M >= 256) return launch_cfg<256, 256, 32, 4, 2, 2, A_T, B_KN, EPI>(fn, a, s);
+        return launch_cfg<64, 128, 64, 3, 2, 2, A_T, B_KN, EPI>(fn, a, s);
+    }
 }
 
 static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb,
