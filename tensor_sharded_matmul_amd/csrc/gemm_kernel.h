@@ -10,23 +10,31 @@
 // ([TPSP] "MLP：先列后行": GeLU and SiLU(gate)*up are local, per element).
 //
 // Design (gfx950 / CDNA4):
-//  * WAVES_M x WAVES_N waves of 64 lanes; each wave owns a (BM/WAVES_M) x
-//    (BN/WAVES_N) sub-tile of C in f32 accumulators.
+//  * WAVES_M x WAVES_N waves of 64 lanes, one workgroup per CU. Each wave owns
+//    a (TM/WAVES_M) x (TN/WAVES_N) sub-tile of C in f32 accumulators (AGPRs).
 //  * v_mfma_f32_16x16x32_bf16 with the operands swapped (the MFMA "A" operand
 //    is the B tile), so each lane ends with 4 consecutive columns of one C row
 //    and epilogue stores are 16-byte (f32) or 8-byte (bf16) vectors.
 //  * Operand tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
-//    staging registers), STAGES deep, so STAGES-1 K-steps of loads are in
-//    flight while the MFMAs consume the oldest one; one barrier per K-step.
-//    The loads are issued from inline asm with explicit vmcnt waits, because
-//    the compiler would otherwise drain every LDS-DMA load before each
-//    barrier. Rows past K (and past M / N) read as zero through the buffer
-//    descriptor's range check.
+//    staging registers) into a ring of STAGES buffers of BK k-rows. A stage
+//    is refilled as soon as its MFMA fragments are in registers, so STAGES-1
+//    stages of loads are in flight while one is read. The loads are issued
+//    from inline asm with explicit vmcnt waits (the compiler would otherwise
+//    drain every LDS-DMA load before each barrier). Rows past K (and past
+//    M / N) read as zero through the buffer descriptor's range check.
+//  * Fragments are double-buffered in registers: the LDS reads of k-step
+//    kt+1 are interleaved with the MFMAs of k-step kt (pinned with
+//    sched_group_barrier), so with one wave per SIMD the matrix core does not
+//    wait on LDS latency; one barrier per k-step.
+//  * The loaded tile (BM x BN) may be wider than the computed one (TM x TN):
+//    224-wide computed tiles divide the 3584 / 7168 widths of the Llama-3-70B
+//    shard into a whole number of waves of 256 workgroups, while loads stay in
+//    64-lane-aligned 256-wide rows.
 //  * LDS layouts keep the operand as stored in HBM:
 //      K-contiguous tile [rows][BK]: 16-byte chunk c of row r is stored at
 //        c ^ swz(r), swz(r) = (r>>1)&7 (BK=64) or (r>>2)&3 (BK=32), so the 16
 //        rows one MFMA fragment read touches fall in 16 distinct bank groups
-//        (gfx950 LDS: 64 banks x 4 B, 16 lanes of a ds_read_b128 per clock).
+//        (gfx950 LDS: 64 banks x 4 B).
 //      MN-contiguous tile [BK][cols]: chunk c of k-row k at c ^ (2(k&3) +
 //        8((k>>3)&1)); fragments are read with ds_read_b64_tr_b16, which
 //        transposes 4x4 blocks of 16-bit values across each 16-lane group,
@@ -50,6 +58,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Compile-time loops. Register arrays (accumulators, fragments) are indexed
+// only through these: an index that depends on whether the compiler chose to
+// unroll a loop can demote a whole array to scratch memory, whose accesses
+// would also upset the explicit vmcnt accounting of the LDS-DMA pipeline.
+// ---------------------------------------------------------------------------
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 constexpr int kGroupM = 4;     // tile rows per L2 group
 
@@ -126,11 +148,15 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_
 
 // Wait until at most N of this wave's LDS-DMA loads are outstanding and its LDS
 // reads are done, then barrier: afterwards every wave's loads of the stage the
-// wait covers are in LDS, and no wave still reads the stage about to be refilled.
+// wait covers are in LDS, and no wave still reads a stage about to be refilled.
+// The LDS-read drain is issued as a builtin so that the compiler's own wait
+// tracking knows every LDS read is complete after it (an asm wait is opaque to
+// it and it would then stall on reads issued after the barrier).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -141,10 +167,14 @@ __device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)addr);
 }
 
-__device__ __forceinline__ bf16x8_t lds_read_tr2(uint32_t addr0, uint32_t addr1) {
+// One 16x32 MFMA operand block from an MN-contiguous tile of C columns: two
+// ds_read_b64_tr_b16, the second 4 k-rows further on (the swizzle of k-row
+// k + 4 equals that of k for the rows a fragment touches, see mntile_frag_addr).
+template <int C>
+__device__ __forceinline__ bf16x8_t lds_read_tr2(uint32_t addr) {
     typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr0);
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr1);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(addr + 4 * C * 2));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -165,23 +195,29 @@ struct IdentityCols {
     }
 };
 
-// SwiGLU B tile: each wave column of WN tile columns holds WN/2 gate columns
-// followed by the WN/2 up columns of the same F indices.
-template <int WN>
+// SwiGLU B tile of HALF + HALF loaded columns: the first half holds gate
+// columns z0 .. z0+HALF-1, the second the up columns of the same F indices.
+template <int HALF>
 struct SwigluCols {
     int z0, f;
     __device__ __forceinline__ int operator()(int c) const {
-        const int wc = c / WN;
-        const int p = c % WN;
-        const int j = z0 + wc * (WN / 2) + (p % (WN / 2));
+        const int p = c % HALF;
+        const int j = z0 + p;
         if (j >= f) return 0;  // outputs past f are never stored
-        return p < WN / 2 ? j : f + j;
+        return c < HALF ? j : f + j;
     }
 };
 
 // ---------------------------------------------------------------------------
 // Per-lane DMA offsets of one operand tile (bytes, relative to the matrix).
 // ---------------------------------------------------------------------------
+
+// Keep a loop-invariant 32-bit value in one VGPR. Without this the compiler
+// forms such offsets with a 64-bit multiply-add, keeps both halves live across
+// the k-loop and spills them; a spill reload inside the loop waits for every
+// outstanding LDS-DMA load.
+__device__ __forceinline__ void pin32(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 
 // K-contiguous operand [rows][K]: tile [R][BK].
 template <int R, int BK, int NWAVES>
@@ -194,20 +230,20 @@ struct KTileDma {
     uint32_t off[kPerWave];
 
     __device__ __forceinline__ void init(int wave, int lane, int row0, int ld) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
+        static_for<0, kPerWave>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
             const int I = wave * kPerWave + i;
             const int row = I * kRpi + lane / kCpr;
             const int c = (lane % kCpr) ^ swz_k<BK>(row);
             off[i] = (uint32_t)(row0 + row) * (uint32_t)ld * 2u + (uint32_t)c * 16u;
-        }
+            pin32(off[i]);
+        });
     }
-    __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t lds_tile, int wave, uint32_t kbytes) const {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i)
-            dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
+    // load i of this wave's share of the tile (1 KB of LDS per load)
+    __device__ __forceinline__ void issue_one(int i, i32x4_t rsrc, uint32_t lds_tile, int wave,
+                                              uint32_t kbytes) const {
+        dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
     }
-    static constexpr uint32_t step_bytes(int /*ld*/) { return BK * 2; }
 };
 
 // MN-contiguous operand [K][cols]: tile [BK][C].
@@ -223,18 +259,19 @@ struct MNTileDma {
 
     template <class ColMap>
     __device__ __forceinline__ void init(int wave, int lane, int ld, const ColMap& colmap) {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i) {
+        static_for<0, kPerWave>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
             const int I = wave * kPerWave + i;
             const int k = I * kRpi + lane / kCpr;
             const int c = (lane % kCpr) ^ swz_mn(k);
             off[i] = (uint32_t)k * (uint32_t)ld * 2u + (uint32_t)colmap(c * 8) * 2u;
-        }
+            pin32(off[i]);
+        });
     }
-    __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t lds_tile, int wave, uint32_t kbytes) const {
-#pragma unroll
-        for (int i = 0; i < kPerWave; ++i)
-            dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
+    // load i of this wave's share of the tile (1 KB of LDS per load)
+    __device__ __forceinline__ void issue_one(int i, i32x4_t rsrc, uint32_t lds_tile, int wave,
+                                              uint32_t kbytes) const {
+        dma16(rsrc, off[i] + kbytes, lds_tile + (uint32_t)(wave * kPerWave + i) * 1024u);
     }
 };
 
@@ -247,180 +284,238 @@ __device__ __forceinline__ uint32_t ktile_frag_addr(uint32_t tile, int rb, int s
     return tile + (uint32_t)(row * BK * 2 + c * 16);
 }
 
-// The two ds_read_b64_tr_b16 addresses of a 16x32 operand block whose index
-// (column of the [BK][C] tile) runs over cb..cb+15, k32 step s.
+// Address of the first of the two ds_read_b64_tr_b16 of a 16x32 operand block
+// whose index (column of the [BK][C] tile) runs over cb..cb+15, k32 step s.
+// Lane (x, g) reads k-rows k0 = 32 s + 8 g + (x >> 2) and k0 + 4; both have
+// the same swizzle (k0 & 3 and bit 3 of k0 agree), so the second read is the
+// first plus 4 rows.
 template <int C>
-__device__ __forceinline__ void mntile_frag_addr(uint32_t tile, int cb, int s, int lane, uint32_t& a0,
-                                                 uint32_t& a1) {
+__device__ __forceinline__ uint32_t mntile_frag_addr(uint32_t tile, int cb, int s, int lane) {
     const int x = lane & 15, g = lane >> 4;
     const int col = cb + 4 * (x & 3);
     const int k0 = 32 * s + 8 * g + (x >> 2);
-    const int k1 = k0 + 4;
     const int c0 = (col >> 3) ^ swz_mn(k0);
-    const int c1 = (col >> 3) ^ swz_mn(k1);
     const int h = (col & 7) * 2;  // 0 or 8 bytes inside the chunk
-    a0 = tile + (uint32_t)(k0 * C * 2 + c0 * 16 + h);
-    a1 = tile + (uint32_t)(k1 * C * 2 + c1 * 16 + h);
+    return tile + (uint32_t)(k0 * C * 2 + c0 * 16 + h);
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue: lane holds C[m][n .. n+3] of each 16x16 block (i, j).
+// Epilogue: lane holds C[m][n .. n+3] of each 16x16 block (i, j). mb: row of
+// block i = 0 for this lane; nb: first column of block j = 0 (SWIGLU: of the
+// gate block j = 0; the up block j + NI/2 covers the same output columns).
+// Rows are handled one at a time (sched_barrier) to bound live registers.
 // ---------------------------------------------------------------------------
-template <int MI, int NI, int WM, int WN, int EPI>
-__device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int m0,
-                                         int n0, int wm, int wn, int lr, int lq) {
-    const int mb = m0 + wm * WM + lr;
-    if constexpr (EPI == EPI_F32) {
-        float* C = reinterpret_cast<float*>(args.C);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = mb + i * 16;
-            if (m >= args.M) continue;
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int n = n0 + wn * WN + j * 16 + lq * 4;
-                if (n >= args.N) continue;
-                f32x4_t* p = reinterpret_cast<f32x4_t*>(C + (size_t)m * args.ldc + n);
-                f32x4_t v = acc[i][j];
-                if (args.accumulate) v += *p;
-                *p = v;
-            }
-        }
-    } else if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU) {
-        uint16_t* C = reinterpret_cast<uint16_t*>(args.C);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = mb + i * 16;
-            if (m >= args.M) continue;
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int n = n0 + wn * WN + j * 16 + lq * 4;
-                if (n >= args.N) continue;
-                const f32x4_t v = acc[i][j];
-                u32x2_t o;
-                if constexpr (EPI == EPI_GELU) {
-                    o[0] = pack_bf16x2(gelu_f(v[0]), gelu_f(v[1]));
-                    o[1] = pack_bf16x2(gelu_f(v[2]), gelu_f(v[3]));
-                    if (args.C2) {
-                        u32x2_t h;
-                        h[0] = pack_bf16x2(v[0], v[1]);
-                        h[1] = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<u32x2_t*>(args.C2 + (size_t)m * args.ldc2 + n) = h;
-                    }
-                } else {
-                    o[0] = pack_bf16x2(v[0], v[1]);
-                    o[1] = pack_bf16x2(v[2], v[3]);
-                }
-                *reinterpret_cast<u32x2_t*>(C + (size_t)m * args.ldc + n) = o;
-            }
-        }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        uint16_t* C = reinterpret_cast<uint16_t*>(args.C);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = mb + i * 16;
-            if (m >= args.M) continue;
-#pragma unroll
-            for (int j = 0; j < NI / 2; ++j) {
-                const int n = n0 + wn * (WN / 2) + j * 16 + lq * 4;
-                if (n >= args.N) continue;
-                const f32x4_t g = acc[i][j];
-                const f32x4_t u = acc[i][j + NI / 2];
-                float z[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z[r] = g[r] * sigmoid_f(g[r]) * u[r];
-                u32x2_t o;
-                o[0] = pack_bf16x2(z[0], z[1]);
-                o[1] = pack_bf16x2(z[2], z[3]);
-                *reinterpret_cast<u32x2_t*>(C + (size_t)m * args.ldc + n) = o;
-                if (args.C2) {
-                    u32x2_t hg, hu;
-                    hg[0] = pack_bf16x2(g[0], g[1]);
-                    hg[1] = pack_bf16x2(g[2], g[3]);
-                    hu[0] = pack_bf16x2(u[0], u[1]);
-                    hu[1] = pack_bf16x2(u[2], u[3]);
-                    uint16_t* hrow = args.C2 + (size_t)m * args.ldc2;
-                    *reinterpret_cast<u32x2_t*>(hrow + n) = hg;
-                    *reinterpret_cast<u32x2_t*>(hrow + args.f + n) = hu;
-                }
-            }
-        }
-    } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) {
-        uint16_t* C = reinterpret_cast<uint16_t*>(args.C);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = mb + i * 16;
-            if (m >= args.M) continue;
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int n = n0 + wn * WN + j * 16 + lq * 4;
-                if (n >= args.N) continue;
-                const f32x4_t dz = acc[i][j];
-                const uint16_t* hrow = args.aux + (size_t)m * args.ldc2;
-                uint16_t* crow = C + (size_t)m * args.ldc;
-                if constexpr (EPI == EPI_GELU_BWD) {
-                    const u32x2_t a = *reinterpret_cast<const u32x2_t*>(hrow + n);
-                    float x[4] = {bf16_bits_to_f32(a[0] & 0xffffu), bf16_bits_to_f32(a[0] >> 16),
-                                  bf16_bits_to_f32(a[1] & 0xffffu), bf16_bits_to_f32(a[1] >> 16)};
-                    u32x2_t o;
-                    o[0] = pack_bf16x2(dz[0] * gelu_grad_f(x[0]), dz[1] * gelu_grad_f(x[1]));
-                    o[1] = pack_bf16x2(dz[2] * gelu_grad_f(x[2]), dz[3] * gelu_grad_f(x[3]));
-                    *reinterpret_cast<u32x2_t*>(crow + n) = o;
-                } else {
-                    const u32x2_t gb = *reinterpret_cast<const u32x2_t*>(hrow + n);
-                    const u32x2_t ub = *reinterpret_cast<const u32x2_t*>(hrow + args.f + n);
-                    float g[4] = {bf16_bits_to_f32(gb[0] & 0xffffu), bf16_bits_to_f32(gb[0] >> 16),
-                                  bf16_bits_to_f32(gb[1] & 0xffffu), bf16_bits_to_f32(gb[1] >> 16)};
-                    float u[4] = {bf16_bits_to_f32(ub[0] & 0xffffu), bf16_bits_to_f32(ub[0] >> 16),
-                                  bf16_bits_to_f32(ub[1] & 0xffffu), bf16_bits_to_f32(ub[1] >> 16)};
-                    float dg[4], du[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float s = sigmoid_f(g[r]);
-                        du[r] = dz[r] * g[r] * s;
-                        dg[r] = dz[r] * u[r] * (s + g[r] * s * (1.0f - s));
-                    }
-                    u32x2_t og, ou;
-                    og[0] = pack_bf16x2(dg[0], dg[1]);
-                    og[1] = pack_bf16x2(dg[2], dg[3]);
-                    ou[0] = pack_bf16x2(du[0], du[1]);
-                    ou[1] = pack_bf16x2(du[2], du[3]);
-                    *reinterpret_cast<u32x2_t*>(crow + n) = og;
-                    *reinterpret_cast<u32x2_t*>(crow + args.f + n) = ou;
-                }
-            }
-        }
-    }
+__device__ __forceinline__ u32x2_t pack4(float a, float b, float c, float d) {
+    u32x2_t o;
+    o[0] = pack_bf16x2(a, b);
+    o[1] = pack_bf16x2(c, d);
+    return o;
 }
+
+__device__ __forceinline__ void unpack4(u32x2_t v, float (&x)[4]) {
+    x[0] = bf16_bits_to_f32(v[0] & 0xffffu);
+    x[1] = bf16_bits_to_f32(v[0] >> 16);
+    x[2] = bf16_bits_to_f32(v[1] & 0xffffu);
+    x[3] = bf16_bits_to_f32(v[1] >> 16);
+}
+
+template <int MI, int NI, int EPI>
+__device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb, int nb) {
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int m = mb + i * 16;
+        if (m < args.M) {
+            if constexpr (EPI == EPI_F32) {
+                f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb);
+                if (args.accumulate) {
+                    static_for<0, NI>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        if (nb + j * 16 < args.N) row[j * 4] = acc[i][j] + row[j * 4];
+                    });
+                } else {
+                    static_for<0, NI>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        if (nb + j * 16 < args.N) row[j * 4] = acc[i][j];
+                    });
+                }
+            } else if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU) {
+                uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
+                static_for<0, NI>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int n = nb + j * 16;
+                    if (n < args.N) {
+                        const f32x4_t v = acc[i][j];
+                        if constexpr (EPI == EPI_GELU) {
+                            *reinterpret_cast<u32x2_t*>(crow + n) =
+                                pack4(gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+                            if (args.C2)
+                                *reinterpret_cast<u32x2_t*>(args.C2 + (size_t)m * args.ldc2 + n) =
+                                    pack4(v[0], v[1], v[2], v[3]);
+                        } else {
+                            *reinterpret_cast<u32x2_t*>(crow + n) = pack4(v[0], v[1], v[2], v[3]);
+                        }
+                    }
+                });
+            } else if constexpr (EPI == EPI_SWIGLU) {
+                uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
+                static_for<0, NI / 2>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int n = nb + j * 16;
+                    if (n < args.N) {
+                        const f32x4_t g = acc[i][j];
+                        const f32x4_t u = acc[i][j + NI / 2];
+                        float z[4];
+                        static_for<0, 4>([&](auto rc) {
+                            constexpr int r = decltype(rc)::value;
+                            z[r] = g[r] * sigmoid_f(g[r]) * u[r];
+                        });
+                        *reinterpret_cast<u32x2_t*>(crow + n) = pack4(z[0], z[1], z[2], z[3]);
+                        if (args.C2) {
+                            uint16_t* hrow = args.C2 + (size_t)m * args.ldc2;
+                            *reinterpret_cast<u32x2_t*>(hrow + n) = pack4(g[0], g[1], g[2], g[3]);
+                            *reinterpret_cast<u32x2_t*>(hrow + args.f + n) = pack4(u[0], u[1], u[2], u[3]);
+                        }
+                    }
+                });
+            } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) {
+                uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
+                const uint16_t* hrow = args.aux + (size_t)m * args.ldc2;
+                static_for<0, NI>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int n = nb + j * 16;
+                    if (n < args.N) {
+                        const f32x4_t dz = acc[i][j];
+                        if constexpr (EPI == EPI_GELU_BWD) {
+                            float x[4];
+                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + n), x);
+                            *reinterpret_cast<u32x2_t*>(crow + n) =
+                                pack4(dz[0] * gelu_grad_f(x[0]), dz[1] * gelu_grad_f(x[1]),
+                                      dz[2] * gelu_grad_f(x[2]), dz[3] * gelu_grad_f(x[3]));
+                        } else {
+                            float g[4], u[4], dg[4], du[4];
+                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + n), g);
+                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + args.f + n), u);
+                            static_for<0, 4>([&](auto rc) {
+                                constexpr int r = decltype(rc)::value;
+                                const float sg = sigmoid_f(g[r]);
+                                du[r] = dz[r] * g[r] * sg;
+                                dg[r] = dz[r] * u[r] * (sg + g[r] * sg * (1.0f - sg));
+                            });
+                            *reinterpret_cast<u32x2_t*>(crow + n) = pack4(dg[0], dg[1], dg[2], dg[3]);
+                            *reinterpret_cast<u32x2_t*>(crow + args.f + n) = pack4(du[0], du[1], du[2], du[3]);
+                        }
+                    }
+                });
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Tile configuration.
+//   BM x BN   loaded operand tiles (LDS); TM x TN computed tile (TM <= BM,
+//             TN <= BN); for SWIGLU, TN counts gate and up columns (TN/2 of
+//             each, output tile TN/2 wide) and BN/2 columns of each half are
+//             loaded
+//   BKA, SA   k-rows per stage and stages of the A operand's LDS ring
+//   BKB, SB   the same for B
+// A K-contiguous operand is staged 64 k-rows at a time: each tile row is then
+// one whole 128-byte line (rows of half a line halve the rate at which the
+// load unit returns data). An MN-contiguous operand has whole lines at any
+// depth and uses 32-row stages, so that more of them fit in flight.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int TM_, int TN_, int BKA_, int SA_, int BKB_, int SB_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, TM = TM_, TN = TN_;
+    static constexpr int BKA = BKA_, SA = SA_, BKB = BKB_, SB = SB_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+};
+
+// ---------------------------------------------------------------------------
+// The LDS-DMA issue order, as a compile-time model. The k-loop runs in k32
+// sub-steps u; operand o (0 = A, 1 = B) has stages of p_o sub-steps in a ring
+// of S_o buffers. The buffer of stage s is free once the reads of its last
+// sub-step are done, i.e. at the barrier of sub-step (s + 1) p_o - 1, where
+// stage s + S_o is issued into it: stage s is issued at sub-step
+// t_o(s) = (s - S_o + 1) p_o - 1 (A before B within a sub-step), and the
+// prologue issues every stage with t_o(s) < 0 in that same order, so the
+// sequence is periodic from the start. At the barrier of sub-step u the
+// fragments of sub-step u + 1 are needed: stages (u + 1) / p_o. vmcnt counts
+// this wave's loads in issue order, so the wait allows the loads issued after
+// the last needed one to stay outstanding.
+// ---------------------------------------------------------------------------
+// Issue slots inside a sub-step: NOPS memory operations (NDMA LDS-DMA loads,
+// NRD fragment reads) spread evenly over the first W of its NMFMA MFMAs, the
+// loads evenly among the reads. Bursts of loads (all waves leave a barrier
+// together) would queue at the CU's address unit and stall every wave's
+// in-order MFMA stream behind them.
+template <int NMFMA, int NDMA, int NRD>
+struct Slots {
+    static constexpr int NOPS = NDMA + NRD;
+    static constexpr int W = NMFMA * 7 / 8 > 0 ? NMFMA * 7 / 8 : 1;
+    // operations k in [begin(m), begin(m + 1)) follow MFMA m
+    static constexpr int begin(int m) { return (m * NOPS + W - 1) / W; }
+    static constexpr int MAXPER = (NOPS + W - 1) / W + 1;
+    // loads before operation k, and whether operation k is a load
+    static constexpr int loads_before(int k) { return NDMA == 0 ? 0 : (k * NDMA + NOPS - 1) / NOPS; }
+    static constexpr bool is_load(int k) {
+        return NDMA > 0 && loads_before(k) < NDMA && loads_before(k) * NOPS / NDMA == k;
+    }
+};
+
+struct RingModel {
+    int pA, SA, LA, pB, SB, LB;
+    constexpr int t_of(int o, int st) const { return o == 0 ? (st - SA + 1) * pA - 1 : (st - SB + 1) * pB - 1; }
+    constexpr int key(int o, int st) const { return 2 * t_of(o, st) + o; }
+    // loads this wave may leave outstanding at the barrier of sub-step u
+    constexpr int wait_count(int u) const {
+        const int ka = key(0, (u + 1) / pA), kb = key(1, (u + 1) / pB);
+        const int kmax = ka > kb ? ka : kb;
+        int x = 0;
+        for (int st = 0; t_of(0, st) < u; ++st)
+            if (key(0, st) > kmax) x += LA;
+        for (int st = 0; t_of(1, st) < u; ++st)
+            if (key(1, st) > kmax) x += LB;
+        return x;
+    }
+    // does operand o issue a stage at sub-step u (u >= 0)?
+    constexpr bool issues(int o, int u) const { return (u + 1) % (o == 0 ? pA : pB) == 0; }
+};
 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_T, bool B_KN, int EPI>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+template <class CF, bool A_T, bool B_KN, int EPI>
+__global__ void __launch_bounds__(64 * CF::WAVES_M * CF::WAVES_N)
 gemm_kernel(const GemmArgs args) {
+    constexpr int BM = CF::BM, BN = CF::BN, TM = CF::TM, TN = CF::TN;
+    constexpr int BKA = CF::BKA, SA = CF::SA, BKB = CF::BKB, SB = CF::SB;
+    constexpr int WAVES_M = CF::WAVES_M, WAVES_N = CF::WAVES_N;
     constexpr int NWAVES = WAVES_M * WAVES_N;
-    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    constexpr int MI = WM / 16, NI = WN / 16;
     constexpr bool SWIGLU = (EPI == EPI_SWIGLU);
-    constexpr int BNZ = SWIGLU ? BN / 2 : BN;  // output columns per tile
-    constexpr int STAGE_BYTES = (BM + BN) * BK * 2;
+    constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
+    constexpr int MI = WM / 16, NI = WN / 16;
+    constexpr int PA = BKA / 32, PB = BKB / 32;     // k32 sub-steps per stage
+    constexpr int TNZ = SWIGLU ? TN / 2 : TN;       // output columns per tile
+    constexpr int A_STAGE = BM * BKA * 2, B_STAGE = BN * BKB * 2;
+    static_assert(TM <= BM && TN <= BN, "computed tile must fit the loaded tile");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
-    static_assert(!SWIGLU || (NI % 2 == 0 && B_KN), "SwiGLU needs an even gate/up split");
-    static_assert(STAGES >= 2, "at least two stages");
+    static_assert((BKA == 32 || BKA == 64) && (BKB == 32 || BKB == 64), "stages of 32 or 64 k-rows");
+    static_assert(!SWIGLU || (NI % 2 == 0 && B_KN && WN % 32 == 0), "SwiGLU needs an even gate/up split");
+    static_assert(SA >= 2 && SB >= 2, "at least two stages per ring");
+    static_assert(SA * A_STAGE + SB * B_STAGE <= 160 * 1024, "gfx950 LDS is 160 KB");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SA * A_STAGE + SB * B_STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int lr = lane & 15, lq = lane >> 4;
 
     // --- tile index (XCD-aware, grouped) ---
-    const int tiles_m = (args.M + BM - 1) / BM;
-    const int tiles_n = (args.N + BNZ - 1) / BNZ;
+    const int tiles_m = (args.M + TM - 1) / TM;
+    const int tiles_n = (args.N + TNZ - 1) / TNZ;
     const int T = tiles_m * tiles_n;
     const int bid = blockIdx.x;
     const int per = T >> 3;
@@ -431,14 +526,14 @@ gemm_kernel(const GemmArgs args) {
     const int in_group = lid % (kGroupM * tiles_n);
     const int tm = first_m + in_group % gsz;
     const int tn = in_group / gsz;
-    const int m0 = tm * BM;
-    const int n0 = tn * BNZ;
+    const int m0 = tm * TM;
+    const int n0 = tn * TNZ;
 
     // --- DMA descriptors and per-lane offsets ---
     const i32x4_t rsA = make_rsrc(args.A, args.a_bytes);
     const i32x4_t rsB = make_rsrc(args.B, args.b_bytes);
-    using ADma = typename std::conditional<A_T, MNTileDma<BM, BK, NWAVES>, KTileDma<BM, BK, NWAVES>>::type;
-    using BDma = typename std::conditional<B_KN, MNTileDma<BN, BK, NWAVES>, KTileDma<BN, BK, NWAVES>>::type;
+    using ADma = typename std::conditional<A_T, MNTileDma<BM, BKA, NWAVES>, KTileDma<BM, BKA, NWAVES>>::type;
+    using BDma = typename std::conditional<B_KN, MNTileDma<BN, BKB, NWAVES>, KTileDma<BN, BKB, NWAVES>>::type;
     ADma da;
     BDma db;
     if constexpr (A_T) {
@@ -448,92 +543,225 @@ gemm_kernel(const GemmArgs args) {
     }
     if constexpr (B_KN) {
         if constexpr (SWIGLU) {
-            db.init(wave, lane, args.ldb, SwigluCols<WN>{n0, args.f});
+            db.init(wave, lane, args.ldb, SwigluCols<BN / 2>{n0, args.f});
         } else {
             db.init(wave, lane, args.ldb, IdentityCols{n0, args.N});
         }
     } else {
         db.init(wave, lane, n0, args.ldb);
     }
-    const uint32_t a_step = A_T ? (uint32_t)BK * (uint32_t)args.lda * 2u : (uint32_t)BK * 2u;
-    const uint32_t b_step = B_KN ? (uint32_t)BK * (uint32_t)args.ldb * 2u : (uint32_t)BK * 2u;
-    const uint32_t lds0 = lds_addr(smem);
-    constexpr int LOADS_PER_STAGE = ADma::kPerWave + BDma::kPerWave;
+    const uint32_t a_step = A_T ? (uint32_t)BKA * (uint32_t)args.lda * 2u : (uint32_t)BKA * 2u;
+    const uint32_t b_step = B_KN ? (uint32_t)BKB * (uint32_t)args.ldb * 2u : (uint32_t)BKB * 2u;
+    const uint32_t ldsA = lds_addr(smem), ldsB = ldsA + SA * A_STAGE;
+    constexpr int LA = ADma::kPerWave, LB = BDma::kPerWave;  // loads per stage per wave
+    constexpr RingModel ring{PA, SA, LA, PB, SB, LB};
 
-    auto issue = [&](int kt) {
-        const uint32_t st = lds0 + (uint32_t)((kt % STAGES) * STAGE_BYTES);
-        da.issue(rsA, st, wave, (uint32_t)kt * a_step);
-        db.issue(rsB, st + BM * BK * 2, wave, (uint32_t)kt * b_step);
+    // load d of this wave's share of a stage of operand A / B: LDS buffer at
+    // byte offset `buf` of the ring, k-rows starting at byte offset `kb`
+    auto issue_a = [&](auto dc, uint32_t buf, uint32_t kb) {
+        da.issue_one(decltype(dc)::value, rsA, ldsA + buf, wave, kb);
+    };
+    auto issue_b = [&](auto dc, uint32_t buf, uint32_t kb) {
+        db.issue_one(decltype(dc)::value, rsB, ldsB + buf, wave, kb);
     };
 
-    // --- fragment base addresses (stage 0) ---
-    uint32_t fa[MI][BK / 32][2];
-    uint32_t fb[NI][BK / 32][2];
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            if constexpr (A_T) {
-                mntile_frag_addr<BM>(lds0, wm * WM + 16 * i, s, lane, fa[i][s][0], fa[i][s][1]);
-            } else {
-                fa[i][s][0] = ktile_frag_addr<BK>(lds0, wm * WM + 16 * i, s, lane);
-                fa[i][s][1] = 0;
-            }
+    // --- fragment addresses in buffer 0 of each ring ---
+    // B column of fragment j inside the loaded tile
+    auto bcol = [&](int j) -> int {
+        if constexpr (SWIGLU) {
+            return j < NI / 2 ? wn * (WN / 2) + 16 * j : BN / 2 + wn * (WN / 2) + 16 * (j - NI / 2);
+        } else {
+            return wn * WN + 16 * j;
         }
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            if constexpr (B_KN) {
-                mntile_frag_addr<BN>(lds0 + BM * BK * 2, wn * WN + 16 * j, s, lane, fb[j][s][0], fb[j][s][1]);
-            } else {
-                fb[j][s][0] = ktile_frag_addr<BK>(lds0 + BM * BK * 2, wn * WN + 16 * j, s, lane);
-                fb[j][s][1] = 0;
-            }
-        }
-    }
+    };
+    // K-contiguous fragments of one wave differ by whole 16-row blocks, whose
+    // swizzle is the same, so they are a base address plus a constant (folded
+    // into the LDS instruction's offset); MN-contiguous ones need one address
+    // per fragment. Index h: k32 half of a 64-row stage.
+    uint32_t fa[MI][PA];
+    uint32_t fb[NI][PB];
+    static_for<0, PA>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const uint32_t a_base = ktile_frag_addr<BKA>(ldsA, wm * WM, h, lane);
+        static_for<0, MI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (A_T) fa[i][h] = mntile_frag_addr<BM>(ldsA, wm * WM + 16 * i, h, lane);
+            else fa[i][h] = a_base + (uint32_t)(i * 16 * BKA * 2);
+        });
+    });
+    static_for<0, PB>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const uint32_t b_base = ktile_frag_addr<BKB>(ldsB, wn * WN, h, lane);
+        static_for<0, NI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (B_KN) fb[j][h] = mntile_frag_addr<BN>(ldsB, bcol(j), h, lane);
+            else fb[j][h] = b_base + (uint32_t)(j * 16 * BKB * 2);
+        });
+    });
 
     f32x4_t acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    static_for<0, MI>([&](auto ic) {
+        static_for<0, NI>([&](auto jc) {
+            acc[decltype(ic)::value][decltype(jc)::value] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        });
+    });
 
-    const int KT = (args.K + BK - 1) / BK;
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < KT) issue(st);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + STAGES - 2 < KT) {
-            wait_vmcnt_barrier<(STAGES - 2) * LOADS_PER_STAGE>();
+    // Fragments of one k32 sub-step: the wave's MI A blocks and NI B blocks.
+    struct Frags {
+        bf16x8_t a[MI];
+        bf16x8_t b[NI];
+    };
+    // Fragment read r (0 <= r < NFR) of a sub-step whose A data sits at LDS
+    // offset soa (half ha of the A stage) and B data at sob (half hb): the
+    // wave's A blocks, then its B blocks.
+    constexpr int NFR = MI + NI;
+    auto read_one = [&](Frags& fr, auto rc, uint32_t soa, uint32_t sob, auto hac, auto hbc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int ha = decltype(hac)::value, hb = decltype(hbc)::value;
+        if constexpr (r < MI) {
+            if constexpr (A_T) fr.a[r] = lds_read_tr2<BM>(fa[r][ha] + soa);
+            else fr.a[r] = lds_read16(fa[r][ha] + soa);
         } else {
-            wait_vmcnt_barrier<0>();
+            if constexpr (B_KN) fr.b[r - MI] = lds_read_tr2<BN>(fb[r - MI][hb] + sob);
+            else fr.b[r - MI] = lds_read16(fb[r - MI][hb] + sob);
         }
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    };
+    // MFMA m (0 <= m < NMFMA) of a sub-step, A block major. The accumulator is
+    // tied to its AGPRs (inline asm): the builtin leaves the register
+    // allocator free to pick an untied destination, and it then copies
+    // accumulators between AGPRs and VGPRs on every k-step.
+    constexpr int NMFMA = MI * NI;
+    auto mfma_one = [&acc](const Frags& fr, auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int i = m / NI, j = m % NI;
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fr.b[j]), "v"(fr.a[i]));
+    };
+    static_assert(NMFMA >= LA + LB, "fewer MFMAs than loads per sub-step");
 
-        const uint32_t so = (uint32_t)((kt % STAGES) * STAGE_BYTES);
-#pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            bf16x8_t af[MI], bfr[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                if constexpr (A_T) af[i] = lds_read_tr2(fa[i][s][0] + so, fa[i][s][1] + so);
-                else af[i] = lds_read16(fa[i][s][0] + so);
-            }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                if constexpr (B_KN) bfr[j] = lds_read_tr2(fb[j][s][0] + so, fb[j][s][1] + so);
-                else bfr[j] = lds_read16(fb[j][s][0] + so);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    // the waits the model derives are the same for every sub-step of a parity
+    static_assert(ring.wait_count(0) == ring.wait_count(2) && ring.wait_count(2) == ring.wait_count(4) &&
+                      ring.wait_count(1) == ring.wait_count(3) && ring.wait_count(3) == ring.wait_count(5),
+                  "LDS-DMA waits are not periodic");
+    static_assert(ring.wait_count(0) <= 63 && ring.wait_count(1) <= 63, "vmcnt range");
+
+    // k32 sub-steps, an even count (the register double buffer alternates per
+    // sub-step and the loop runs pairs). NN / NT contract over a model width,
+    // a multiple of 64: nothing is added. TN contracts over tokens: k-rows
+    // past K read as zeros (buffer range check).
+    const int U = ((args.K + 63) / 64) * 2;
+
+    // Ring positions (uniform, kept in scalar registers and advanced with a
+    // compare-and-wrap, no division): the buffer the next fragment reads
+    // come from, the buffer the next load goes to, and that load's k offset.
+    uint32_t a_rd = 0, b_rd = 0, a_wr = 0, b_wr = 0;
+    uint32_t a_kb = (uint32_t)SA * a_step, b_kb = (uint32_t)SB * b_step;
+    auto wrap_a = [](uint32_t x) { x += A_STAGE; return x == (uint32_t)(SA * A_STAGE) ? 0u : x; };
+    auto wrap_b = [](uint32_t x) { x += B_STAGE; return x == (uint32_t)(SB * B_STAGE) ? 0u : x; };
+
+    // Sub-step of parity PAR: MFMAs on `cur` while the fragments of the next
+    // sub-step are read into `nxt`. If a ring starts a new stage with the next
+    // sub-step, this sub-step first waits for it (and for every wave to have
+    // read the buffer that stage's predecessor left, which it then refills).
+    // Loads are issued for every stage, also past the last one: those read
+    // past K (range-checked) into buffers no later read uses, which keeps the
+    // waits constant; the last sub-step's fragment reads likewise fetch data
+    // nothing uses. Loads and reads are spread over the MFMAs (Slots); the
+    // sched_barrier fences keep that order.
+    auto substep = [&](auto parc, Frags& cur, Frags& nxt) {
+        constexpr int PAR = decltype(parc)::value;
+        constexpr bool IA = ring.issues(0, PAR), IB = ring.issues(1, PAR);
+        constexpr int NDA = IA ? LA : 0, NDMA = NDA + (IB ? LB : 0);
+        using SL = Slots<NMFMA, NDMA, NFR>;
+        constexpr int HA = (PAR + 1) % PA, HB = (PAR + 1) % PB;  // halves the reads fetch
+        if constexpr (IA || IB) {
+            wait_vmcnt_barrier<ring.wait_count(PAR)>();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (IA) a_rd = wrap_a(a_rd);
+        if constexpr (IB) b_rd = wrap_b(b_rd);
+        const uint32_t soa = a_rd, sob = b_rd, wa = a_wr, wb = b_wr, ka = a_kb, kb = b_kb;
+        static_for<0, NMFMA>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            mfma_one(cur, mc);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, SL::MAXPER>([&](auto cc) {
+                constexpr int k = SL::begin(m) + decltype(cc)::value;
+                if constexpr (k < SL::begin(m + 1) && k < SL::NOPS) {
+                    if constexpr (SL::is_load(k)) {
+                        constexpr int d = SL::loads_before(k);
+                        if constexpr (d < NDA) issue_a(std::integral_constant<int, d>{}, wa, ka);
+                        else issue_b(std::integral_constant<int, d - NDA>{}, wb, kb);
+                    } else {
+                        read_one(nxt, std::integral_constant<int, k - SL::loads_before(k)>{}, soa, sob,
+                                 std::integral_constant<int, HA>{}, std::integral_constant<int, HB>{});
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+        });
+        if constexpr (IA) { a_wr = wrap_a(a_wr); a_kb += a_step; }
+        if constexpr (IB) { b_wr = wrap_b(b_wr); b_kb += b_step; }
+    };
+
+    if (U > 0) {  // K = 0 (no tokens in a weight gradient): C = 0
+        // prologue: the stages issued "before sub-step 0", in the model's
+        // order, then sub-step 0's fragments go to registers
+        static_for<0, 2 * (SA * PA + SB * PB) + 4>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;         // key - kmin
+            constexpr int kmin = 2 * (-(SA > SB ? SA : SB) * (PA > PB ? PA : PB) - 2);
+            constexpr int key = k + kmin;
+            if constexpr (key < 0) {
+                constexpr int o = ((key % 2) + 2) % 2;      // operand of this key
+                constexpr int t = (key - o) / 2;            // its sub-step
+                // stage st with t_o(st) == t, if any and if st >= 0
+                constexpr int pp = o == 0 ? PA : PB, SS = o == 0 ? SA : SB;
+                if constexpr ((t + 1) % pp == 0 && (t + 1) / pp + SS - 1 >= 0) {
+                    constexpr int st = (t + 1) / pp + SS - 1;
+                    if constexpr (o == 0)
+                        static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), (uint32_t)st * a_step); });
+                    else
+                        static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), (uint32_t)st * b_step); });
+                }
+            }
+        });
+        // stage 0 of both rings landed: every load issued after the later of
+        // the two may stay outstanding
+        constexpr int W0 = [] {
+            constexpr RingModel rm{PA, SA, LA, PB, SB, LB};
+            const int kmax = rm.key(0, 0) > rm.key(1, 0) ? rm.key(0, 0) : rm.key(1, 0);
+            int x = 0;
+            for (int st = 0; rm.t_of(0, st) < 0; ++st)
+                if (rm.key(0, st) > kmax) x += LA;
+            for (int st = 0; rm.t_of(1, st) < 0; ++st)
+                if (rm.key(1, st) > kmax) x += LB;
+            return x;
+        }();
+        wait_vmcnt_barrier<W0>();
+        Frags f0, f1;
+        static_for<0, NFR>([&](auto rc) {
+            read_one(f0, rc, 0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        });
+        // the accumulators were zeroed by VALU writes, which the first MFMA
+        // (inline asm, invisible to the hazard checks) must not overtake
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 4" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < U; u += 2) {
+            substep(std::integral_constant<int, 0>{}, f0, f1);
+            substep(std::integral_constant<int, 1>{}, f1, f0);
+        }
+        // MFMA results are read by the epilogue only after the longest
+        // MFMA-write -> read wait (the checks do not see the asm MFMAs), and
+        // after every LDS-DMA load has retired
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    epilogue<MI, NI, WM, WN, EPI>(acc, args, m0, n0, wm, wn, lr, lq);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int mb = m0 + wm * WM + lr;
+    const int nb = n0 + wn * (SWIGLU ? WN / 2 : WN) + lq * 4;
+    epilogue<MI, NI, EPI>(acc, args, mb, nb);
 }
 
 }  // namespace tps
