@@ -19,7 +19,7 @@ Tensors are returned as ``uint16`` arrays holding the bfloat16 bit patterns;
 
 The shapes are Llama-3-70B's (h=8192, n_h=64, n_kv=8, d_h=128, F=28672) at
 TP degree 8, a GPT-style layer (h=4096, F=16384) at TP degree 4, and a tiny
-layer for exhaustive checks, as listed in the workload table of the design doc.
+layer for exhaustive checks (the WORKLOADS table below).
 """
 from __future__ import annotations
 

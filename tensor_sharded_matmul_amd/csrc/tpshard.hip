@@ -17,7 +17,7 @@ namespace tps {
 // ---------------------------------------------------------------------------
 static thread_local std::string g_last_error;
 
-static tp_status fail(tp_status st, const char* fmt, ...) {
+tp_status fail(tp_status st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -84,112 +84,10 @@ static tp_status check_elems(const char* fn, int64_t rows, int64_t cols) {
 // ---------------------------------------------------------------------------
 // GEMM dispatch
 // ---------------------------------------------------------------------------
-template <class CF, bool A_T, bool B_KN, int EPI>
-static tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
-    constexpr int TNZ = (EPI == EPI_SWIGLU) ? CF::TN / 2 : CF::TN;
-    const long long tiles = (long long)((a.M + CF::TM - 1) / CF::TM) * ((a.N + TNZ - 1) / TNZ);
-    if (tiles == 0) return TP_OK;
-    if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-    hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI>), dim3((unsigned)tiles),
-                       dim3(64 * CF::WAVES_M * CF::WAVES_N), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-    return TP_OK;
-}
-
-// Operands are addressed with 32-bit byte offsets (buffer descriptors).
-static constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
-
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
-
-// Large-tile shapes: one workgroup of 4 waves per CU, 256-wide loaded tiles.
-// The computed tile is 256 x 256, 256 x 224 or 224 x 256, whichever needs the
-// least (waves of workgroups) x (tile area): 224 divides the 3584 / 7168 MLP
-// widths of a Llama-3-70B shard into whole waves over 256 CUs.
-// LDS rings per operand layout: K-contiguous operands in stages of 64 k-rows
-// (a tile row is one whole 128-byte line), MN-contiguous ones in 32-row
-// stages. Depths are the fastest measured on MI355X for the Llama-3-70B
-// shard products (a deeper ring or the full 160 KB of LDS did not help).
-template <bool A_T, bool B_KN>
-struct Rings;
-template <>
-struct Rings<false, true> {  // NN: A K-contiguous, B MN-contiguous (128 KB)
-    static constexpr int BKA = 64, SA = 2, BKB = 32, SB = 4;
-};
-template <>
-struct Rings<false, false> {  // NT: both K-contiguous (128 KB)
-    static constexpr int BKA = 64, SA = 2, BKB = 64, SB = 2;
-};
-template <>
-struct Rings<true, true> {  // TN: both MN-contiguous (112 KB)
-    static constexpr int BKA = 32, SA = 4, BKB = 32, SB = 3;
-};
-
-template <bool A_T, bool B_KN, int BM, int BN, int TM, int TN, int WVM, int WVN>
-using CfgOf = Cfg<BM, BN, TM, TN, Rings<A_T, B_KN>::BKA, Rings<A_T, B_KN>::SA, Rings<A_T, B_KN>::BKB,
-                  Rings<A_T, B_KN>::SB, WVM, WVN>;
-
-enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224 };
-
-static Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224) {
-    const long long cus = device_cus();
-    auto cost = [&](int tm, int tnz, int area) {
-        const long long t = (long long)((M + tm - 1) / tm) * ((Nout + tnz - 1) / tnz);
-        return ((t + cus - 1) / cus) * area;
-    };
-    Shape best = SHAPE_SQ;
-    long long c_best = cost(256, swiglu ? 128 : 256, 256 * 256);
-    const long long c_n = cost(256, swiglu ? 112 : 224, 256 * 224);
-    if (c_n < c_best) { best = SHAPE_N224; c_best = c_n; }
-    if (allow_m224 && !swiglu) {
-        const long long c_m = cost(224, 256, 224 * 256);
-        if (c_m < c_best) { best = SHAPE_M224; c_best = c_m; }
-    }
-    return best;
-}
-
+// GEMM launches: defined in gemm_launch.h and instantiated, one layout and
+// epilogue family per file, in the gemm_*.hip sources (compiled in parallel).
 template <bool A_T, bool B_KN, int EPI>
-static tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
-    if (a.M == 0 || a.N == 0) return TP_OK;
-    const int64_t a_bytes = (int64_t)(A_T ? a.K : a.M) * a.lda * 2;
-    const int64_t b_bytes = (int64_t)(B_KN ? a.K : a.N) * a.ldb * 2;
-    if (a_bytes > kMaxOperandBytes || b_bytes > kMaxOperandBytes)
-        return fail(TP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
-    a.a_bytes = (uint32_t)a_bytes;
-    a.b_bytes = (uint32_t)b_bytes;
-    constexpr bool SW = (EPI == EPI_SWIGLU);
-    using Sq = CfgOf<A_T, B_KN, 256, 256, 256, 256, 2, 2>;
-    using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
-    using M224 = CfgOf<A_T, B_KN, 256, 256, 224, 256, 2, 2>;
-    using SwiN224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 4, 1>;  // SwiGLU: 112 gate + 112 up columns
-    if constexpr (!A_T) {
-        // few token rows: 64 x 128 tiles, a smaller ring of the same shape
-        using Small = Cfg<64, 128, 64, 128, 64, 3, Rings<A_T, B_KN>::BKB, B_KN ? 4 : 3, 2, 2>;
-        if (a.M < 256) return launch_cfg<Small, A_T, B_KN, EPI>(fn, a, s);
-    }
-    switch (pick_shape(a.M, a.N, SW, true)) {
-        case SHAPE_N224:
-            if constexpr (SW) return launch_cfg<SwiN224, A_T, B_KN, EPI>(fn, a, s);
-            else return launch_cfg<N224, A_T, B_KN, EPI>(fn, a, s);
-        case SHAPE_M224:
-            if constexpr (!SW) return launch_cfg<M224, A_T, B_KN, EPI>(fn, a, s);
-            else return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
-        default:
-            return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
-    }
-}
+tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s);
 
 static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb,
                           int ldc) {

@@ -68,7 +68,7 @@ def _tiny_gelu():
 
 
 def test_tiny_gelu_sum_of_shard_partials_equals_unsharded():
-    # configs[0]-style: t=4 shards of GeLU(X A_i) B_i summed equal GeLU(X A) B
+    # the tiny workload: t=4 shards of GeLU(X A_i) B_i summed equal GeLU(X A) B
     w, d = _tiny_gelu()
     X, A, B = d["X"], d["W_in"], d["W_out"]
     full = O.gelu(X @ A) @ B
