@@ -12,9 +12,15 @@ Also measured in the same run (reported under "rows"): every single-kernel
 GEMM of the step (HIP events on the stream the kernels run on), the fused-QKV
 regroup (GB/s, buffers rotated past the 256 MB Infinity Cache), the attention
 projections (QKV + W_O) forward and backward at N = 4096 and decode at N = 16,
-and the GPT-style GeLU MLP shard (N = 8192, h = 4096, F = 16384, t = 4). The
+the GPT-style GeLU MLP shard (N = 8192, h = 4096, F = 16384, t = 4), and, as
+context, the ROCm BLAS library (torch.matmul) on the step's GEMM shapes. The
 fp64 oracle is timed on a bounded token sample of the same MLP workload on the
 host cores (cpu_baseline).
+
+roofline: the step's dominant kernel (largest single launch), its FLOPs per
+launch over its average launch time (HIP events over back-to-back launches),
+against the bf16 dense peak; traffic: its HBM bytes per launch from the
+committed counter summary (profiles/), if taken on the current kernel sources.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -31,6 +37,43 @@ PEAK_HBM_GBS = 8000.0         # HBM3E
 METRIC = "TFLOP/s + % bf16 MFMA peak, Llama-3-70B TP=8 MLP shard fwd+bwd, 1 GPU"
 
 
+# What each timed product launches (one gemm_kernel instantiation each).
+KERNEL_DESC = {
+    "gemm1_gate_up_swiglu": "gemm_kernel NN, 256x224 tile (112 gate + 112 up columns), SwiGLU epilogue",
+    "gemm2_down_partial": "gemm_kernel NN, 256x256 tile, fp32 store",
+    "bwd_dx_partial": "gemm_kernel NT, 256x256 tile, fp32 store",
+    "bwd_dw_gate_up": "gemm_kernel TN, 256x224 tile, fp32 store",
+    "bwd_dw_down": "gemm_kernel TN, 224x256 tile, fp32 store",
+}
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_dominant_kernel.json")
+
+
+def kernel_sources_sha() -> str:
+    """Hash of the kernel sources, to tell whether recorded counters are current."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(product: str):
+    """HBM bytes per launch of `product` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a copy of known size), or None if
+    there is none for this product or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("product") != product or t.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -44,6 +87,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="token sample for the oracle CPU baseline (0 = skip)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device 5 times (scale for HBM byte counters), then exit")
     return ap.parse_args()
 
 
@@ -64,6 +109,14 @@ def main() -> int:
         return 1
     T.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} bytes 5 times")
+        return 0
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
 
@@ -146,45 +199,46 @@ def main() -> int:
         f"{100 * value / PEAK_BF16_TFLOPS:.1f}% of peak  (wall {wall:.3f}s)")
 
     # ---------------- per-kernel timings (single-kernel entry points) ----------------
+    # Each entry point below launches exactly the kernel (same template
+    # instantiation and launch shape) that the step launches for that product.
     kern = {
-        "gemm1_gate_up_swiglu": (lambda: T.tp_col_linear(X, W_in, "swiglu", Y=Z, H_save=H),
-                                 "gemm_kernel<256, 256, false, true, 3>"),
-        "gemm2_down_partial": (lambda: T.tp_row_linear_partial(Z, W_out, P=P),
-                               "gemm_kernel<256, 256, false, true, 0>"),
-        "bwd_dx_partial": (lambda: T.tp_col_linear_bwd(X, W_in, dH, dX_part=dX, want_dw=False),
-                           "gemm_kernel<256, 256, false, false, 0>"),
-        "bwd_dw_gate_up": (lambda: T.tp_col_linear_bwd(X, W_in, dH, dW=dWi, want_dx=False),
-                           "gemm_kernel<256, 256, true, true, 0>"),
-        "bwd_dw_down": (lambda: T.tp_row_linear_bwd(Z, W_out, dY, dW=dWo, want_dz=False),
-                        "gemm_kernel<256, 256, true, true, 0>"),
+        "gemm1_gate_up_swiglu": lambda: T.tp_col_linear(X, W_in, "swiglu", Y=Z, H_save=H),
+        "gemm2_down_partial": lambda: T.tp_row_linear_partial(Z, W_out, P=P),
+        "bwd_dx_partial": lambda: T.tp_col_linear_bwd(X, W_in, dH, dX_part=dX, want_dw=False),
+        "bwd_dw_gate_up": lambda: T.tp_col_linear_bwd(X, W_in, dH, dW=dWi, want_dx=False),
+        "bwd_dw_down": lambda: T.tp_row_linear_bwd(Z, W_out, dY, dW=dWo, want_dz=False),
     }
     kt = {}
-    for name, (fn, kname) in kern.items():
+    for name, fn in kern.items():
         mean, med, mn = time_fn(fn, args.reps)
-        kt[name] = {"kernel": kname, "ms": round(mean, 4), "ms_median": round(med, 4),
+        kt[name] = {"ms": round(mean, 4), "ms_median": round(med, 4),
                     "tflops": round(fl[name] / (mean * 1e-3) / 1e12, 1)}
         log(f"[bench] {name:24s} {mean:.4f} ms  {kt[name]['tflops']} TFLOP/s")
     bwd_mean = time_fn(bwd, args.reps)[0]
     dz_ms = bwd_mean - sum(kt[k]["ms"] for k in ("bwd_dx_partial", "bwd_dw_gate_up", "bwd_dw_down"))
-    kt["bwd_dz_swiglu"] = {"kernel": "gemm_kernel<256, 256, false, false, 5>",
-                           "ms": round(dz_ms, 4), "derived": "bwd total minus the other three",
+    kt["bwd_dz_swiglu"] = {"ms": round(dz_ms, 4), "derived": "bwd total minus the other three",
                            "tflops": round(fl["bwd_dz_swiglu"] / (dz_ms * 1e-3) / 1e12, 1)}
 
-    # dominant kernel: the largest share of the step; per-launch average of that kernel
-    by_kernel = {}
-    for name, r in kt.items():
-        e = by_kernel.setdefault(r["kernel"], {"ms": 0.0, "flops": 0, "launches": 0})
-        e["ms"] += r["ms"]
-        e["flops"] += fl[name]
-        e["launches"] += 1
-    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
-    per_launch_flops = dom["flops"] / dom["launches"]
-    per_launch_ms = dom["ms"] / dom["launches"]
-    achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "flops_per_launch": per_launch_flops, "avg_launch_ms": round(per_launch_ms, 4)}
+    # dominant kernel: the single launch with the largest share of the step,
+    # timed over `reps` back-to-back launches on the launch stream
+    dom = max((n for n in kern), key=lambda n: kt[n]["ms"])
+    fn = kern[dom]
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = e0.elapsed_time(e1) / args.reps
+    achieved = fl[dom] / (per_launch_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": committed_traffic(dom), "kernel": KERNEL_DESC[dom],
+                "flop_per_launch": fl[dom], "avg_launch_ms": round(per_launch_ms, 4)}
+    log(f"[bench] dominant {dom}: {per_launch_ms:.4f} ms per launch, {achieved:.1f} TFLOP/s")
 
     rows = {"mlp_kernels": kt,
             "fwd_ms": round(time_fn(fwd, args.reps)[0], 4), "bwd_ms": round(bwd_mean, 4)}
@@ -194,6 +248,7 @@ def main() -> int:
     del Z, H, P, dH, dX, dWi, dWo
     if not args.no_rows:
         rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, args.reps))
+        rows["vendor_gemm_reference"] = vendor_reference(torch, dev, time_fn, args.reps, N, h, f)
     torch.cuda.synchronize()
 
     # ---------------- CPU baseline: the oracle on a token sample ----------------
@@ -306,6 +361,25 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, reps):
     ms = time_fn(lambda: T.tp_mlp_shard_fwd(Xg, Ag, Bg, "gelu", Z=Zg, H_save=Hg, P=Pg), reps)[0]
     res["gpt_gelu_mlp_fwd_t4"] = {"ms": round(ms, 4), "gflop": round(flg / 1e9, 2),
                                   "tflops": round(flg / (ms * 1e-3) / 1e12, 1)}
+    return res
+
+
+def vendor_reference(torch, dev, time_fn, reps, N, h, f):
+    """Context only: torch.matmul (the ROCm BLAS library) on the step's GEMM
+    shapes, bf16 in and out, plain product without the epilogues. Not part of
+    the measured path."""
+    shapes = {"gemm1_gate_up": (N, h, 2 * f), "gemm2_down": (N, f, h), "dx": (N, 2 * f, h),
+              "dw_gate_up": (h, N, 2 * f), "dw_down": (f, N, h)}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = {}
+    for name, (M, K, Nn) in shapes.items():
+        a = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
+        b = torch.randn((K, Nn), device=dev, generator=g).to(torch.bfloat16)
+        ms = time_fn(lambda: a @ b, reps)[0]
+        res[name] = {"ms": round(ms, 4), "tflops": round(2 * M * K * Nn / (ms * 1e-3) / 1e12, 1)}
+        del a, b
+    log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()))
     return res
 
 
