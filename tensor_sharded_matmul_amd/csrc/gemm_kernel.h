@@ -96,6 +96,10 @@ struct GemmArgs {
     int f;           // SWIGLU / SWIGLU_BWD: column offset of the "up" half
     int accumulate;  // EPI_F32: add into C
     uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (buffer range check)
+    // Split-K: ksplit workgroups per output tile, each contracting kper rows
+    // of K (a multiple of 64; the last split ends at K); split s writes its
+    // fp32 partial to C + s * M * ldc. ksplit = 1: the whole K, C as given.
+    int ksplit, kper;
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
@@ -517,7 +521,8 @@ gemm_kernel(const GemmArgs args) {
     const int tiles_m = (args.M + TM - 1) / TM;
     const int tiles_n = (args.N + TNZ - 1) / TNZ;
     const int T = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
+    const int split = (int)(blockIdx.x % (unsigned)args.ksplit);
+    const int bid = (int)(blockIdx.x / (unsigned)args.ksplit);
     const int per = T >> 3;
     const int lid = (bid < per * 8) ? (bid & 7) * per + (bid >> 3) : bid;
     const int group = lid / (kGroupM * tiles_n);
@@ -529,9 +534,15 @@ gemm_kernel(const GemmArgs args) {
     const int m0 = tm * TM;
     const int n0 = tn * TNZ;
 
+    // --- this workgroup's K range (split-K) ---
+    const int k0 = split * args.kper;
+    const int Kloc = args.ksplit > 1 ? min(args.K, k0 + args.kper) - k0 : args.K;
+    const uint32_t a_k0 = (uint32_t)k0 * (A_T ? (uint32_t)args.lda : 1u) * 2u;  // bytes
+    const uint32_t b_k0 = (uint32_t)k0 * (B_KN ? (uint32_t)args.ldb : 1u) * 2u;
+
     // --- DMA descriptors and per-lane offsets ---
-    const i32x4_t rsA = make_rsrc(args.A, args.a_bytes);
-    const i32x4_t rsB = make_rsrc(args.B, args.b_bytes);
+    const i32x4_t rsA = make_rsrc(reinterpret_cast<const uint8_t*>(args.A) + a_k0, args.a_bytes - a_k0);
+    const i32x4_t rsB = make_rsrc(reinterpret_cast<const uint8_t*>(args.B) + b_k0, args.b_bytes - b_k0);
     using ADma = typename std::conditional<A_T, MNTileDma<BM, BKA, NWAVES>, KTileDma<BM, BKA, NWAVES>>::type;
     using BDma = typename std::conditional<B_KN, MNTileDma<BN, BKB, NWAVES>, KTileDma<BN, BKB, NWAVES>>::type;
     ADma da;
@@ -648,7 +659,7 @@ gemm_kernel(const GemmArgs args) {
     // sub-step and the loop runs pairs). NN / NT contract over a model width,
     // a multiple of 64: nothing is added. TN contracts over tokens: k-rows
     // past K read as zeros (buffer range check).
-    const int U = ((args.K + 63) / 64) * 2;
+    const int U = ((Kloc + 63) / 64) * 2;
 
     // Ring positions (uniform, kept in scalar registers and advanced with a
     // compare-and-wrap, no division): the buffer the next fragment reads
@@ -761,7 +772,16 @@ gemm_kernel(const GemmArgs args) {
     const int lr = lane & 15, lq = lane >> 4;
     const int mb = m0 + wm * WM + lr;
     const int nb = n0 + wn * (SWIGLU ? WN / 2 : WN) + lq * 4;
-    epilogue<MI, NI, EPI>(acc, args, mb, nb);
+    if constexpr (EPI == EPI_F32) {  // split-K partials are plain fp32 stores
+        GemmArgs part = args;
+        if (args.ksplit > 1) {
+            part.C = reinterpret_cast<float*>(args.C) + (size_t)split * args.M * args.ldc;
+            part.accumulate = 0;
+        }
+        epilogue<MI, NI, EPI_F32>(acc, part, mb, nb);
+    } else {
+        epilogue<MI, NI, EPI>(acc, args, mb, nb);
+    }
 }
 
 }  // namespace tps

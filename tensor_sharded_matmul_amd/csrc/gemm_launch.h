@@ -17,7 +17,7 @@ tp_status fail(tp_status st, const char* fmt, ...);
 template <class CF, bool A_T, bool B_KN, int EPI>
 inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
     constexpr int TNZ = (EPI == EPI_SWIGLU) ? CF::TN / 2 : CF::TN;
-    const long long tiles = (long long)((a.M + CF::TM - 1) / CF::TM) * ((a.N + TNZ - 1) / TNZ);
+    const long long tiles = (long long)((a.M + CF::TM - 1) / CF::TM) * ((a.N + TNZ - 1) / TNZ) * a.ksplit;
     if (tiles == 0) return TP_OK;
     if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
     hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI>), dim3((unsigned)tiles),
@@ -30,24 +30,9 @@ inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
 // Operands are addressed with 32-bit byte offsets (buffer descriptors).
 static constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
 
-// Compute units of the current device (cached per device).
-inline int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cus[dev] = v;
-    }
-    return cus[dev];
-}
+// Compute units of the current device (cached per device; tpshard.hip).
+int device_cus();
 
-// Large-tile shapes: one workgroup of 4 waves per CU, 256-wide loaded tiles.
-// The computed tile is 256 x 256, 256 x 224 or 224 x 256, whichever needs the
-// least (waves of workgroups) x (tile area): 224 divides the 3584 / 7168 MLP
-// widths of a Llama-3-70B shard into whole waves over 256 CUs.
 // LDS rings per operand layout: K-contiguous operands in stages of 64 k-rows
 // (a tile row is one whole 128-byte line), MN-contiguous ones in 32-row
 // stages. Depths are the fastest measured on MI355X for the Llama-3-70B

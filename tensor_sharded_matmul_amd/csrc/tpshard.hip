@@ -2,10 +2,14 @@
 // selection and launch for every entry point declared in include/tpshard.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/tpshard.h"
 #include "gemm_kernel.h"
@@ -102,7 +106,152 @@ static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, i
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
+    a.ksplit = 1;
+    a.kper = K;
     return a;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K for products with few token rows (decode). A forward product with
+// M <= 64 rows has too few output tiles to keep 256 CUs streaming its weight
+// from HBM, so K is split over workgroups: each writes an fp32 partial of the
+// whole [M, n_w] product to a workspace, and splitk_reduce sums the partials
+// and applies the epilogue (store, accumulate, GeLU, SwiGLU).
+// The workspace belongs to the library: one buffer per (device, stream),
+// grown on demand (hipMalloc outside any kernel; kept until the process
+// ends), so calls on different streams never share one.
+// ---------------------------------------------------------------------------
+static std::mutex g_ws_mutex;
+static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+static tp_status workspace(const char* fn, hipStream_t s, size_t bytes, float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto& w = g_ws[{dev, s}];
+    if (w.second < bytes) {
+        if (w.first) {
+            // earlier work on this stream may still read the old buffer
+            e = hipStreamSynchronize(s);
+            if (e == hipSuccess) e = hipFree(w.first);
+            if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: workspace release: %s", fn, hipGetErrorString(e));
+            w = {nullptr, 0};
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: workspace of %zu bytes: %s", fn, bytes, hipGetErrorString(e));
+        w = {p, bytes};
+    }
+    *out = static_cast<float*>(w.first);
+    return TP_OK;
+}
+
+// out[m][n..n+3] from the sum over splits of ws[s][m][*]. A wave covers
+// 64 / S output quads (4 columns each) with S lanes per quad, S the smallest
+// power of two >= min(ksplit, 64): lane si of a group adds splits si, si + S,
+// ..., the S partial sums are combined with butterfly shuffles, and lane 0 of
+// the group applies the epilogue. EPI_SWIGLU: ws holds [gate | up] (2 f
+// columns).
+template <int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ ws, int ksplit, int S, int M,
+                                                     int Nw, int Nout, void* C, int ldc, uint16_t* C2,
+                                                     int ldc2, int f, int accumulate) {
+    const int lane = threadIdx.x & 63;
+    const int si = lane % S;
+    const int q = Nout / 4;
+    const int64_t total = (int64_t)M * q;
+    const int64_t quads_per_block = (int64_t)(blockDim.x / 64) * (64 / S);
+    const int64_t first = (int64_t)blockIdx.x * quads_per_block + (threadIdx.x / 64) * (64 / S) + lane / S;
+    const size_t split_stride = (size_t)M * Nw;
+    for (int64_t idx = first; idx - lane / S < total; idx += (int64_t)gridDim.x * quads_per_block) {
+        const bool live = idx < total;  // every lane runs the shuffles
+        const int m = live ? (int)(idx / q) : 0, n = live ? (int)(idx % q) * 4 : 0;
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            for (int sp = si; sp < ksplit; sp += S) {
+                const float* row = ws + sp * split_stride + (size_t)m * Nw;
+                v += *reinterpret_cast<const f32x4_t*>(row + n);
+                if constexpr (EPI == EPI_SWIGLU) u += *reinterpret_cast<const f32x4_t*>(row + f + n);
+            }
+        }
+        for (int off = S / 2; off > 0; off /= 2) {
+            for (int r = 0; r < 4; ++r) {
+                v[r] += __shfl_xor(v[r], off, 64);
+                if constexpr (EPI == EPI_SWIGLU) u[r] += __shfl_xor(u[r], off, 64);
+            }
+        }
+        if (!live || si != 0) continue;
+        if constexpr (EPI == EPI_F32) {
+            f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(C) + (size_t)m * ldc + n);
+            *p = accumulate ? *p + v : v;
+        } else if constexpr (EPI == EPI_BF16) {
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + n) = pack4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_GELU) {
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + n) =
+                pack4(gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+            if (C2) *reinterpret_cast<u32x2_t*>(C2 + (size_t)m * ldc2 + n) = pack4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            float z[4];
+            for (int r = 0; r < 4; ++r) z[r] = v[r] * sigmoid_f(v[r]) * u[r];
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(C) + (size_t)m * ldc + n) = pack4(z[0], z[1], z[2], z[3]);
+            if (C2) {
+                *reinterpret_cast<u32x2_t*>(C2 + (size_t)m * ldc2 + n) = pack4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<u32x2_t*>(C2 + (size_t)m * ldc2 + f + n) = pack4(u[0], u[1], u[2], u[3]);
+            }
+        }
+    }
+}
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Forward product (NN) with its epilogue: split-K when the problem has few
+// token rows and few output tiles, else one launch of the tiled kernel.
+// `a` describes the product as for launch_gemm<false, true, EPI> (for
+// SWIGLU: N = f output columns, B has 2 f columns).
+template <int EPI>
+static tp_status forward_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0) return TP_OK;
+    const int Nw = EPI == EPI_SWIGLU ? 2 * a.N : a.N;  // columns of the product
+    const long long tiles = (long long)((a.M + 63) / 64) * ((Nw + 127) / 128);
+    const long long cus = device_cus();
+    if (a.M > 64 || tiles >= 2 * cus || a.K < 256) return launch_gemm<false, true, EPI>(fn, a, s);
+    int ksplit = (int)std::min<long long>((4 * cus + tiles - 1) / tiles, a.K / 128);
+    int kper = ((a.K + ksplit - 1) / ksplit + 63) / 64 * 64;
+    ksplit = (a.K + kper - 1) / kper;
+    if (ksplit < 2) return launch_gemm<false, true, EPI>(fn, a, s);
+    float* ws = nullptr;
+    TP_TRY(workspace(fn, s, (size_t)ksplit * a.M * Nw * sizeof(float), &ws));
+    GemmArgs p = a;
+    p.C = ws;
+    p.ldc = Nw;
+    p.N = Nw;
+    p.C2 = nullptr;
+    p.accumulate = 0;
+    p.ksplit = ksplit;
+    p.kper = kper;
+    TP_TRY((launch_gemm<false, true, EPI_F32>(fn, p, s)));
+    int S = 1;
+    while (S < ksplit && S < 64) S *= 2;
+    const long long quads = (long long)a.M * (a.N / 4);
+    const long long per_block = 4 * (64 / S);
+    const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
+    hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, ksplit, S, a.M, Nw, a.N, a.C,
+                       a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return TP_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -167,9 +316,9 @@ tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_
     a.ldc2 = (int)n_w;
     a.f = (int)n_out;
     tp_status st;
-    if (act == TP_ACT_NONE) st = launch_gemm<false, true, EPI_BF16>(fn, a, s);
-    else if (act == TP_ACT_GELU) st = launch_gemm<false, true, EPI_GELU>(fn, a, s);
-    else st = launch_gemm<false, true, EPI_SWIGLU>(fn, a, s);
+    if (act == TP_ACT_NONE) st = forward_gemm<EPI_BF16>(fn, a, s);
+    else if (act == TP_ACT_GELU) st = forward_gemm<EPI_GELU>(fn, a, s);
+    else st = forward_gemm<EPI_SWIGLU>(fn, a, s);
     return st == TP_OK ? ok() : st;
 }
 
@@ -187,7 +336,7 @@ tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t 
     TP_TRY(check_elems(fn, N, n));
     GemmArgs a = make_args(Z, W, P, (int)N, (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
     a.accumulate = accumulate ? 1 : 0;
-    tp_status st = launch_gemm<false, true, EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
+    tp_status st = forward_gemm<EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
     return st == TP_OK ? ok() : st;
 }
 
@@ -215,12 +364,11 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, i
     a.C2 = static_cast<uint16_t*>(H_save);
     a.ldc2 = (int)n_w;
     a.f = (int)f;
-    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, true, EPI_GELU>(fn, a, s)
-                                      : launch_gemm<false, true, EPI_SWIGLU>(fn, a, s);
+    tp_status st = act == TP_ACT_GELU ? forward_gemm<EPI_GELU>(fn, a, s) : forward_gemm<EPI_SWIGLU>(fn, a, s);
     if (st != TP_OK) return st;
     GemmArgs b = make_args(Z, W_out, P, (int)N, (int)h, (int)f, (int)f, (int)h, (int)h);
     b.accumulate = accumulate ? 1 : 0;
-    st = launch_gemm<false, true, EPI_F32>(fn, b, s);
+    st = forward_gemm<EPI_F32>(fn, b, s);
     return st == TP_OK ? ok() : st;
 }
 
