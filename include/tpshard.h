@@ -22,7 +22,17 @@
  *              rounded to nearest even.
  *   Pointers:  device pointers (hipMalloc'd or torch CUDA tensors), 16-byte
  *              aligned. The caller owns every buffer; the library keeps no
- *              pointer after the call returns and allocates nothing.
+ *              pointer to them after the call returns.
+ *   Workspace: the forward GEMMs of tp_col_linear, tp_row_linear_partial and
+ *              tp_mlp_shard_fwd at N <= 64 tokens split K over workgroups and
+ *              sum the f32 partials in a second kernel. Their scratch is one
+ *              device buffer per (device, stream) that the library allocates
+ *              on first use, grows when a larger one is needed (after
+ *              synchronising that stream) and keeps until the process ends:
+ *              at most 4 * min(4 * CUs / tiles, k / 128) * N * n f32 bytes,
+ *              a few MB for model widths. Every other call allocates
+ *              nothing. Calls that overlap on one stream cannot race on it;
+ *              a failed allocation returns TP_ERR_HIP with nothing enqueued.
  *   Sizes:     N (tokens) is any value >= 0 (N = 0 is a no-op). Model widths
  *              (k, n, h, f, k_loc) must be positive multiples of 64.
  *   Streams:   `stream` is a hipStream_t (NULL = the legacy default stream).

@@ -102,6 +102,9 @@ struct GemmArgs {
     int ksplit, kper;
 };
 
+// Token rows of the tile a split-K product of M rows runs with.
+inline int splitk_tile_m(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
@@ -647,7 +650,9 @@ gemm_kernel(const GemmArgs args) {
         constexpr int i = m / NI, j = m % NI;
         asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fr.b[j]), "v"(fr.a[i]));
     };
-    static_assert(NMFMA >= LA + LB, "fewer MFMAs than loads per sub-step");
+    // (decode tiles, at most 32 token rows, stream the weight and are bound
+    // by HBM, not by the MFMA issue; they may load more often than they MFMA)
+    static_assert(NMFMA >= LA + LB || TM <= 32, "fewer MFMAs than loads per sub-step");
 
     // the waits the model derives are the same for every sub-step of a parity
     static_assert(ring.wait_count(0) == ring.wait_count(2) && ring.wait_count(2) == ring.wait_count(4) &&
@@ -717,11 +722,11 @@ gemm_kernel(const GemmArgs args) {
     if (U > 0) {  // K = 0 (no tokens in a weight gradient): C = 0
         // prologue: the stages issued "before sub-step 0", in the model's
         // order, then sub-step 0's fragments go to registers
-        static_for<0, 2 * (SA * PA + SB * PB) + 4>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;         // key - kmin
-            constexpr int kmin = 2 * (-(SA > SB ? SA : SB) * (PA > PB ? PA : PB) - 2);
-            constexpr int key = k + kmin;
-            if constexpr (key < 0) {
+        // (keys run from the earlier of the two stage 0s up to -1)
+        constexpr int kmin = ring.key(0, 0) < ring.key(1, 0) ? ring.key(0, 0) : ring.key(1, 0);
+        static_for<0, -kmin>([&](auto kc) {
+            constexpr int key = decltype(kc)::value + kmin;
+            {
                 constexpr int o = ((key % 2) + 2) % 2;      // operand of this key
                 constexpr int t = (key - o) / 2;            // its sub-step
                 // stage st with t_o(st) == t, if any and if st >= 0

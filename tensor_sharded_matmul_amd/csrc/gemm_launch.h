@@ -27,6 +27,10 @@ inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
     return TP_OK;
 }
 
+#ifndef TPS_DEC_SB
+#define TPS_DEC_SB 8  // stages of the weight ring of the decode tiles
+#endif
+
 // Operands are addressed with 32-bit byte offsets (buffer descriptors).
 static constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
 
@@ -89,6 +93,15 @@ tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
     using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
     using M224 = CfgOf<A_T, B_KN, 256, 256, 224, 256, 2, 2>;
     using SwiN224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 4, 1>;  // SwiGLU: 112 gate + 112 up columns
+    if constexpr (!A_T && B_KN && EPI == EPI_F32) {
+        // split-K partials of a product with few token rows (decode): the
+        // weight streams from HBM through a deep ring of 32-row stages, and
+        // the token tile is no taller than the rows there are
+        using Dec16 = Cfg<16, 128, 16, 128, 64, 4, 32, TPS_DEC_SB, 1, 2>;
+        using Dec32 = Cfg<32, 128, 32, 128, 64, 4, 32, TPS_DEC_SB, 1, 2>;
+        if (a.ksplit > 1 && a.M <= 16) return launch_cfg<Dec16, A_T, B_KN, EPI>(fn, a, s);
+        if (a.ksplit > 1 && a.M <= 32) return launch_cfg<Dec32, A_T, B_KN, EPI>(fn, a, s);
+    }
     if constexpr (!A_T) {
         // few token rows: 64 x 128 tiles, a smaller ring of the same shape
         using Small = Cfg<64, 128, 64, 128, 64, 3, Rings<A_T, B_KN>::BKB, B_KN ? 4 : 3, 2, 2>;

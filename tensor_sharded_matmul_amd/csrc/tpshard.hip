@@ -216,39 +216,68 @@ int device_cus() {
     return cus[dev];
 }
 
-// Forward product (NN) with its epilogue: split-K when the problem has few
-// token rows and few output tiles, else one launch of the tiled kernel.
+// How a forward product (NN) is run: ksplit == 0 means one launch of the
+// tiled kernel; otherwise K is cut into ksplit chunks of kper (a multiple of
+// 64) whose f32 partials take `bytes` of workspace. Split-K is used when the
+// problem has few token rows and too few output tiles to cover the CUs twice.
 // `a` describes the product as for launch_gemm<false, true, EPI> (for
 // SWIGLU: N = f output columns, B has 2 f columns).
+#ifndef TPS_SPLIT_BLOCKS_PER_CU
+#define TPS_SPLIT_BLOCKS_PER_CU 1  // split workgroups aimed at, per CU
+#endif
+#ifndef TPS_SPLIT_MIN_KPER
+#define TPS_SPLIT_MIN_KPER 512  // smallest K chunk of one workgroup
+#endif
+
+struct SplitPlan {
+    int ksplit = 0, kper = 0, Nw = 0;
+    size_t bytes = 0;
+};
+
+static SplitPlan plan_forward(const GemmArgs& a, bool swiglu) {
+    SplitPlan p;
+    p.Nw = swiglu ? 2 * a.N : a.N;  // columns of the product
+    if (a.M == 0 || a.N == 0) return p;
+    const int tm = splitk_tile_m(a.M);
+    const long long tiles = (long long)((a.M + tm - 1) / tm) * ((p.Nw + 127) / 128);
+    const long long cus = device_cus();
+    if (a.M > 64 || tiles >= 2 * cus || a.K < 2 * TPS_SPLIT_MIN_KPER) return p;
+    int ksplit = (int)std::min<long long>((TPS_SPLIT_BLOCKS_PER_CU * cus + tiles - 1) / tiles,
+                                          a.K / TPS_SPLIT_MIN_KPER);
+    const int kper = ((a.K + ksplit - 1) / ksplit + 63) / 64 * 64;
+    ksplit = (a.K + kper - 1) / kper;
+    if (ksplit < 2) return p;
+    p.ksplit = ksplit;
+    p.kper = kper;
+    p.bytes = (size_t)ksplit * a.M * p.Nw * sizeof(float);
+    return p;
+}
+
+// Forward product with its epilogue, run as plan_forward decides. The
+// workspace is taken before anything is enqueued.
 template <int EPI>
 static tp_status forward_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
     if (a.M == 0 || a.N == 0) return TP_OK;
-    const int Nw = EPI == EPI_SWIGLU ? 2 * a.N : a.N;  // columns of the product
-    const long long tiles = (long long)((a.M + 63) / 64) * ((Nw + 127) / 128);
-    const long long cus = device_cus();
-    if (a.M > 64 || tiles >= 2 * cus || a.K < 256) return launch_gemm<false, true, EPI>(fn, a, s);
-    int ksplit = (int)std::min<long long>((4 * cus + tiles - 1) / tiles, a.K / 128);
-    int kper = ((a.K + ksplit - 1) / ksplit + 63) / 64 * 64;
-    ksplit = (a.K + kper - 1) / kper;
-    if (ksplit < 2) return launch_gemm<false, true, EPI>(fn, a, s);
+    const SplitPlan plan = plan_forward(a, EPI == EPI_SWIGLU);
+    if (plan.ksplit == 0) return launch_gemm<false, true, EPI>(fn, a, s);
     float* ws = nullptr;
-    TP_TRY(workspace(fn, s, (size_t)ksplit * a.M * Nw * sizeof(float), &ws));
+    TP_TRY(workspace(fn, s, plan.bytes, &ws));
     GemmArgs p = a;
     p.C = ws;
-    p.ldc = Nw;
-    p.N = Nw;
+    p.ldc = plan.Nw;
+    p.N = plan.Nw;
     p.C2 = nullptr;
     p.accumulate = 0;
-    p.ksplit = ksplit;
-    p.kper = kper;
+    p.ksplit = plan.ksplit;
+    p.kper = plan.kper;
     TP_TRY((launch_gemm<false, true, EPI_F32>(fn, p, s)));
     int S = 1;
-    while (S < ksplit && S < 64) S *= 2;
+    while (S < plan.ksplit && S < 64) S *= 2;
     const long long quads = (long long)a.M * (a.N / 4);
     const long long per_block = 4 * (64 / S);
     const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
-    hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, ksplit, S, a.M, Nw, a.N, a.C,
-                       a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
+    hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, plan.ksplit, S, a.M, plan.Nw,
+                       a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return TP_OK;
@@ -364,10 +393,18 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, i
     a.C2 = static_cast<uint16_t*>(H_save);
     a.ldc2 = (int)n_w;
     a.f = (int)f;
-    tp_status st = act == TP_ACT_GELU ? forward_gemm<EPI_GELU>(fn, a, s) : forward_gemm<EPI_SWIGLU>(fn, a, s);
-    if (st != TP_OK) return st;
     GemmArgs b = make_args(Z, W_out, P, (int)N, (int)h, (int)f, (int)f, (int)h, (int)h);
     b.accumulate = accumulate ? 1 : 0;
+    // both products share the stream's workspace: size it for the larger
+    // before the first launch, so a failed allocation enqueues nothing
+    const size_t ws_bytes =
+        std::max(plan_forward(a, act == TP_ACT_SWIGLU).bytes, plan_forward(b, false).bytes);
+    if (ws_bytes) {
+        float* ws = nullptr;
+        TP_TRY(workspace(fn, s, ws_bytes, &ws));
+    }
+    tp_status st = act == TP_ACT_GELU ? forward_gemm<EPI_GELU>(fn, a, s) : forward_gemm<EPI_SWIGLU>(fn, a, s);
+    if (st != TP_OK) return st;
     st = forward_gemm<EPI_F32>(fn, b, s);
     return st == TP_OK ? ok() : st;
 }

@@ -75,6 +75,41 @@ def test_col_linear_nn_bf16_exact(N, k, n):
     assert torch.all(big[N * n:] == SENTINEL)
 
 
+# Decode-sized products (N <= 64) whose K is split over workgroups: ragged
+# last chunk (4160), many chunks (8192), 16 / 32 / 64-row tiles, accumulate
+# into the partial.
+SHAPES_SPLIT = [(16, 4160, 256), (40, 4160, 128), (64, 8192, 64), (3, 1024, 1280), (24, 2048, 384),
+                (16, 8192, 1280)]
+
+
+@pytest.mark.parametrize("N,k,n", SHAPES_SPLIT)
+def test_split_k_exact(N, k, n):
+    Xb, X = _ints(20, (N, k))
+    Wb, W = _ints(21, (k, n))
+    P0b, P0 = _ints(22, (N, n))
+    big, Y = _canary_bf16((N, n))
+    T.tp_col_linear(to_dev(Xb), to_dev(Wb), "none", Y=Y)
+    P = torch.from_numpy(P0.astype(np.float32)).to("cuda:0")
+    T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb), P=P, accumulate=True)
+    torch.cuda.synchronize()
+    want = O.col_linear(X, W)
+    assert np.array_equal(bits(Y), rne_bf16_bits(want))
+    assert torch.all(big[N * n:] == SENTINEL)
+    assert np.array_equal(f64(P), P0 + O.row_linear_partial(X, W))
+
+
+def test_split_k_workspace_grows_and_shrinks():
+    # one stream, three calls whose split workspaces are small, large, small
+    for i, (N, k, n) in enumerate([(16, 2048, 128), (64, 8192, 256), (8, 1024, 64)]):
+        Xb, X = _ints(30 + i, (N, k))
+        Wb, W = _ints(40 + i, (k, n))
+        big, P = _canary_f32((N, n))
+        T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb), P=P)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(P), O.row_linear_partial(X, W)), (N, k, n)
+        assert torch.all(big[N * n:] == SENTINEL)
+
+
 SHAPES_BWD = [(300, 320, 256), (16, 128, 192), (1, 64, 64), (513, 256, 128), (1000, 64, 512)]
 
 
@@ -109,10 +144,11 @@ def test_row_linear_bwd_exact(N, k, n):
 
 
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
-@pytest.mark.parametrize("N", [1, 300])
-def test_pre_activation_save_is_exact(act, N):
-    # H_save is X W_in rounded once to bf16, including the SwiGLU gate/up interleave
-    h, f = 256, 192
+@pytest.mark.parametrize("N,h", [(1, 256), (300, 256), (16, 2048)])
+def test_pre_activation_save_is_exact(act, N, h):
+    # H_save is X W_in rounded once to bf16, including the SwiGLU gate/up
+    # interleave (N <= 64 runs the split-K reduction's epilogue)
+    f = 192
     n_w = 2 * f if act == "swiglu" else f
     Xb, X = _ints(14, (N, h))
     Wb, W = _ints(15, (h, n_w))
