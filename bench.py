@@ -181,6 +181,35 @@ def main() -> int:
         ts = [a.elapsed_time(b) for a, b in evs]
         return float(np.mean(ts)), float(np.median(ts)), float(np.min(ts))
 
+    def time_graph(fn, calls, replays=8):
+        """Average ms per call of `fn` replayed from a HIP graph: `calls` calls
+        are captured once on a side stream (after two eager warm-up rounds on
+        it, which also create the library's per-stream split-K workspace) and
+        the graph is replayed `replays` times between two events. For
+        launch-bound calls (decode, regroup) this is the GPU time without the
+        Python binding's per-call host cost."""
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(2 * calls):
+                fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(calls):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):  # replay() launches on the current stream
+            e0.record(side)
+            for _ in range(replays):
+                graph.replay()
+            e1.record(side)
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / (calls * replays)
+
     # ---------------- timed region: K steps ----------------
     for _ in range(args.warmup):
         step()
@@ -247,7 +276,7 @@ def main() -> int:
 
     del Z, H, P, dH, dX, dWi, dWo
     if not args.no_rows:
-        rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, args.reps))
+        rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, args.reps))
         rows["vendor_gemm_reference"] = vendor_reference(torch, dev, time_fn, args.reps, N, h, f)
     torch.cuda.synchronize()
 
@@ -273,7 +302,7 @@ def main() -> int:
     return 0
 
 
-def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, reps):
+def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     """The other rows of the hot path, each timed on its own."""
     res = {}
     bf, f32 = torch.bfloat16, torch.float32
@@ -292,9 +321,10 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, reps):
         it[0] += 1
         T.tp_qkv_regroup(srcs[i % 4], n_h, n_kv, d_h, t, (i // 4) % t, W_r=dsts[i % 4])
 
-    ms = time_fn(regroup, max(reps, 32), warm=4)[0]
+    ms_eager = time_fn(regroup, max(reps, 32), warm=4)[0]
+    ms = time_graph(regroup, 32)
     moved = 2 * h * (width // t) * 2
-    res["qkv_regroup"] = {"ms": round(ms, 5), "bytes": moved,
+    res["qkv_regroup"] = {"ms": round(ms, 5), "ms_eager": round(ms_eager, 5), "bytes": moved,
                           "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
     del srcs, dsts
@@ -343,9 +373,10 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, reps):
         T.tp_col_linear(Xd, Wrs[i], "none", Y=Yd)
         T.tp_row_linear_partial(Od, WOs[i], P=Pd)
 
-    ms = time_fn(decode, max(reps, 32), warm=4)[0]
+    ms_eager = time_fn(decode, max(reps, 32), warm=4)[0]
+    ms = time_graph(decode, 16)
     wbytes = 2 * h * (width // t) + 2 * (n_h * d_h // t) * h
-    res["attn_proj_decode_n16"] = {"ms": round(ms, 4), "weight_bytes": wbytes,
+    res["attn_proj_decode_n16"] = {"ms": round(ms, 4), "ms_eager": round(ms_eager, 4), "weight_bytes": wbytes,
                                    "gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
                                    "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
     del Wrs, WOs, X, O, dQKV, dY, W_r, W_O

@@ -62,10 +62,12 @@ using CfgOf = Cfg<BM, BN, TM, TN, Rings<A_T, B_KN>::BKA, Rings<A_T, B_KN>::SA, R
 
 enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224 };
 
-inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224) {
+// Tile shape with the fewest waves of workgroups (ksplit per tile) times
+// tile area, i.e. the least padded work per CU.
+inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int ksplit) {
     const long long cus = device_cus();
     auto cost = [&](int tm, int tnz, int area) {
-        const long long t = (long long)((M + tm - 1) / tm) * ((Nout + tnz - 1) / tnz);
+        const long long t = (long long)((M + tm - 1) / tm) * ((Nout + tnz - 1) / tnz) * ksplit;
         return ((t + cus - 1) / cus) * area;
     };
     Shape best = SHAPE_SQ;
@@ -107,7 +109,7 @@ tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
         using Small = Cfg<64, 128, 64, 128, 64, 3, Rings<A_T, B_KN>::BKB, B_KN ? 4 : 3, 2, 2>;
         if (a.M < 256) return launch_cfg<Small, A_T, B_KN, EPI>(fn, a, s);
     }
-    switch (pick_shape(a.M, a.N, SW, true)) {
+    switch (pick_shape(a.M, a.N, SW, true, a.ksplit)) {
         case SHAPE_N224:
             if constexpr (SW) return launch_cfg<SwiN224, A_T, B_KN, EPI>(fn, a, s);
             else return launch_cfg<N224, A_T, B_KN, EPI>(fn, a, s);

@@ -216,12 +216,19 @@ int device_cus() {
     return cus[dev];
 }
 
-// How a forward product (NN) is run: ksplit == 0 means one launch of the
-// tiled kernel; otherwise K is cut into ksplit chunks of kper (a multiple of
-// 64) whose f32 partials take `bytes` of workspace. Split-K is used when the
-// problem has few token rows and too few output tiles to cover the CUs twice.
-// `a` describes the product as for launch_gemm<false, true, EPI> (for
-// SWIGLU: N = f output columns, B has 2 f columns).
+// How a product is run: ksplit == 0 means one launch of the tiled kernel;
+// otherwise K is cut into ksplit chunks of kper (a multiple of 64) whose f32
+// partials take `bytes` of workspace and splitk_reduce applies the epilogue.
+//  - Few token rows (M <= 64, NN, the decode shapes): the weight is streamed
+//    from HBM by one split workgroup per CU, in chunks of at least
+//    TPS_SPLIT_MIN_KPER rows.
+//  - Large products whose 256 x 256 tiles do not fill the CUs once (the
+//    attention projections' N = 1024 or 1280 shard widths): the split count
+//    that minimises an estimate of tile waves x chunk length plus the
+//    partials' write and read is used.
+// `a` describes the product as for launch_gemm<A_T, B_KN, EPI> (for SWIGLU:
+// N = f output columns, B has 2 f columns). The activation-backward
+// epilogues are never split (their reduce would need H as well).
 #ifndef TPS_SPLIT_BLOCKS_PER_CU
 #define TPS_SPLIT_BLOCKS_PER_CU 1  // split workgroups aimed at, per CU
 #endif
@@ -234,53 +241,109 @@ struct SplitPlan {
     size_t bytes = 0;
 };
 
-static SplitPlan plan_forward(const GemmArgs& a, bool swiglu) {
+static SplitPlan make_plan(const GemmArgs& a, int Nw, int ksplit_wanted) {
     SplitPlan p;
-    p.Nw = swiglu ? 2 * a.N : a.N;  // columns of the product
-    if (a.M == 0 || a.N == 0) return p;
-    const int tm = splitk_tile_m(a.M);
-    const long long tiles = (long long)((a.M + tm - 1) / tm) * ((p.Nw + 127) / 128);
-    const long long cus = device_cus();
-    if (a.M > 64 || tiles >= 2 * cus || a.K < 2 * TPS_SPLIT_MIN_KPER) return p;
-    int ksplit = (int)std::min<long long>((TPS_SPLIT_BLOCKS_PER_CU * cus + tiles - 1) / tiles,
-                                          a.K / TPS_SPLIT_MIN_KPER);
-    const int kper = ((a.K + ksplit - 1) / ksplit + 63) / 64 * 64;
-    ksplit = (a.K + kper - 1) / kper;
-    if (ksplit < 2) return p;
+    p.Nw = Nw;
+    const int kper = ((a.K + ksplit_wanted - 1) / ksplit_wanted + 63) / 64 * 64;
+    const int ksplit = (a.K + kper - 1) / kper;
+    if (ksplit < 2 || (long long)ksplit * a.M * Nw >= (1LL << 31)) return p;
     p.ksplit = ksplit;
     p.kper = kper;
-    p.bytes = (size_t)ksplit * a.M * p.Nw * sizeof(float);
+    p.bytes = (size_t)ksplit * a.M * Nw * sizeof(float);
     return p;
 }
 
-// Forward product with its epilogue, run as plan_forward decides. The
-// workspace is taken before anything is enqueued.
+static SplitPlan plan_split(const GemmArgs& a, bool swiglu, bool nn, bool splittable) {
+    SplitPlan none;
+    none.Nw = swiglu ? 2 * a.N : a.N;  // columns of the product
+    if (a.M == 0 || a.N == 0 || !splittable) return none;
+    const int Nw = none.Nw;
+    const long long cus = device_cus();
+    if (a.M <= 64) {
+        if (!nn) return none;
+        const int tm = splitk_tile_m(a.M);
+        const long long tiles = (long long)((a.M + tm - 1) / tm) * ((Nw + 127) / 128);
+        if (tiles >= 2 * cus || a.K < 2 * TPS_SPLIT_MIN_KPER) return none;
+        const long long want = std::min<long long>((TPS_SPLIT_BLOCKS_PER_CU * cus + tiles - 1) / tiles,
+                                                   a.K / TPS_SPLIT_MIN_KPER);
+        return make_plan(a, Nw, (int)want);
+    }
+    const long long tiles = (long long)((a.M + 255) / 256) * ((Nw + 255) / 256);
+    if (tiles >= cus || a.K < 2048) return none;
+    // seconds: a CU finishes a 256 x 256 x k tile at ~4.6 TFLOP/s; partials
+    // move at ~5 TB/s; the reduce launch costs ~4 us
+    auto estimate = [&](int ksplit, int kper) {
+        const double waves = (double)((tiles * ksplit + cus - 1) / cus);
+        double t = waves * kper * (2.0 * 256 * 256 / 4.6e12);
+        if (ksplit > 1) t += (double)ksplit * a.M * Nw * 8 / 5.0e12 + 4e-6;
+        return t;
+    };
+    int best = 1;
+    double t_best = estimate(1, a.K);
+    for (int want = 2; want <= 16; ++want) {
+        const int kper = ((a.K + want - 1) / want + 63) / 64 * 64;
+        if (kper < 512) break;
+        const int ksplit = (a.K + kper - 1) / kper;
+        const double t = estimate(ksplit, kper);
+        if (t < 0.95 * t_best) {
+            best = ksplit;
+            t_best = t;
+        }
+    }
+    return best > 1 ? make_plan(a, Nw, best) : none;
+}
+
 template <int EPI>
-static tp_status forward_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
-    if (a.M == 0 || a.N == 0) return TP_OK;
-    const SplitPlan plan = plan_forward(a, EPI == EPI_SWIGLU);
-    if (plan.ksplit == 0) return launch_gemm<false, true, EPI>(fn, a, s);
+constexpr bool reducible() {
+    return EPI == EPI_F32 || EPI == EPI_BF16 || EPI == EPI_GELU || EPI == EPI_SWIGLU;
+}
+
+template <bool A_T, bool B_KN, int EPI>
+static SplitPlan plan_of(const GemmArgs& a) {
+    return plan_split(a, EPI == EPI_SWIGLU, !A_T && B_KN, reducible<EPI>());
+}
+
+// Takes the stream's workspace for the largest of a call's plans before the
+// call enqueues anything, so that a failed allocation leaves nothing behind.
+static tp_status reserve(const char* fn, hipStream_t s, std::initializer_list<SplitPlan> plans) {
+    size_t bytes = 0;
+    for (const SplitPlan& p : plans) bytes = std::max(bytes, p.bytes);
+    if (bytes == 0) return TP_OK;
     float* ws = nullptr;
-    TP_TRY(workspace(fn, s, plan.bytes, &ws));
-    GemmArgs p = a;
-    p.C = ws;
-    p.ldc = plan.Nw;
-    p.N = plan.Nw;
-    p.C2 = nullptr;
-    p.accumulate = 0;
-    p.ksplit = plan.ksplit;
-    p.kper = plan.kper;
-    TP_TRY((launch_gemm<false, true, EPI_F32>(fn, p, s)));
-    int S = 1;
-    while (S < plan.ksplit && S < 64) S *= 2;
-    const long long quads = (long long)a.M * (a.N / 4);
-    const long long per_block = 4 * (64 / S);
-    const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
-    hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, plan.ksplit, S, a.M, plan.Nw,
-                       a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-    return TP_OK;
+    return workspace(fn, s, bytes, &ws);
+}
+
+// A product with its epilogue, run as plan_of decides.
+template <bool A_T, bool B_KN, int EPI>
+static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0) return TP_OK;
+    const SplitPlan plan = plan_of<A_T, B_KN, EPI>(a);
+    if (plan.ksplit == 0) return launch_gemm<A_T, B_KN, EPI>(fn, a, s);
+    if constexpr (reducible<EPI>()) {
+        float* ws = nullptr;
+        TP_TRY(workspace(fn, s, plan.bytes, &ws));
+        GemmArgs p = a;
+        p.C = ws;
+        p.ldc = plan.Nw;
+        p.N = plan.Nw;
+        p.C2 = nullptr;
+        p.accumulate = 0;
+        p.ksplit = plan.ksplit;
+        p.kper = plan.kper;
+        TP_TRY((launch_gemm<A_T, B_KN, EPI_F32>(fn, p, s)));
+        int S = 1;
+        while (S < plan.ksplit && S < 64) S *= 2;
+        const long long quads = (long long)a.M * (a.N / 4);
+        const long long per_block = 4 * (64 / S);
+        const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
+        hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, plan.ksplit, S, a.M,
+                           plan.Nw, a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+        return TP_OK;
+    } else {
+        return fail(TP_ERR_UNSUPPORTED, "%s: split of an unsplittable epilogue", fn);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -345,9 +408,9 @@ tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_
     a.ldc2 = (int)n_w;
     a.f = (int)n_out;
     tp_status st;
-    if (act == TP_ACT_NONE) st = forward_gemm<EPI_BF16>(fn, a, s);
-    else if (act == TP_ACT_GELU) st = forward_gemm<EPI_GELU>(fn, a, s);
-    else st = forward_gemm<EPI_SWIGLU>(fn, a, s);
+    if (act == TP_ACT_NONE) st = run_gemm<false, true, EPI_BF16>(fn, a, s);
+    else if (act == TP_ACT_GELU) st = run_gemm<false, true, EPI_GELU>(fn, a, s);
+    else st = run_gemm<false, true, EPI_SWIGLU>(fn, a, s);
     return st == TP_OK ? ok() : st;
 }
 
@@ -365,7 +428,7 @@ tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t 
     TP_TRY(check_elems(fn, N, n));
     GemmArgs a = make_args(Z, W, P, (int)N, (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
     a.accumulate = accumulate ? 1 : 0;
-    tp_status st = forward_gemm<EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
+    tp_status st = run_gemm<false, true, EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
     return st == TP_OK ? ok() : st;
 }
 
@@ -397,15 +460,13 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, i
     b.accumulate = accumulate ? 1 : 0;
     // both products share the stream's workspace: size it for the larger
     // before the first launch, so a failed allocation enqueues nothing
-    const size_t ws_bytes =
-        std::max(plan_forward(a, act == TP_ACT_SWIGLU).bytes, plan_forward(b, false).bytes);
-    if (ws_bytes) {
-        float* ws = nullptr;
-        TP_TRY(workspace(fn, s, ws_bytes, &ws));
-    }
-    tp_status st = act == TP_ACT_GELU ? forward_gemm<EPI_GELU>(fn, a, s) : forward_gemm<EPI_SWIGLU>(fn, a, s);
+    TP_TRY(reserve(fn, s,
+                   {act == TP_ACT_GELU ? plan_of<false, true, EPI_GELU>(a) : plan_of<false, true, EPI_SWIGLU>(a),
+                    plan_of<false, true, EPI_F32>(b)}));
+    tp_status st = act == TP_ACT_GELU ? run_gemm<false, true, EPI_GELU>(fn, a, s)
+                                      : run_gemm<false, true, EPI_SWIGLU>(fn, a, s);
     if (st != TP_OK) return st;
-    st = forward_gemm<EPI_F32>(fn, b, s);
+    st = run_gemm<false, true, EPI_F32>(fn, b, s);
     return st == TP_OK ? ok() : st;
 }
 
@@ -439,21 +500,24 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out, c
     a.aux = static_cast<const uint16_t*>(H_save);
     a.ldc2 = (int)n_w;
     a.f = (int)f;
-    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, false, EPI_GELU_BWD>(fn, a, s)
-                                      : launch_gemm<false, false, EPI_SWIGLU_BWD>(fn, a, s);
-    if (st != TP_OK) return st;
     // dX_part = dH W_in^T (NT)
     GemmArgs b = make_args(dH, W_in, dX_part, (int)N, (int)h, (int)n_w, (int)n_w, (int)n_w, (int)h);
     b.accumulate = accumulate ? 1 : 0;
-    st = launch_gemm<false, false, EPI_F32>(fn, b, s);
-    if (st != TP_OK) return st;
     // dW_in = X^T dH (TN): A = X stored [K=N][M=h], B = dH stored [K=N][n_w]
     GemmArgs c = make_args(X, dH, dW_in, (int)h, (int)n_w, (int)N, (int)h, (int)n_w, (int)n_w);
-    st = launch_gemm<true, true, EPI_F32>(fn, c, s);
-    if (st != TP_OK) return st;
     // dW_out = Z^T dY (TN): A = Z stored [N][f], B = dY stored [N][h]
     GemmArgs d = make_args(Z, dY, dW_out, (int)f, (int)h, (int)N, (int)f, (int)h, (int)h);
-    st = launch_gemm<true, true, EPI_F32>(fn, d, s);
+    TP_TRY(reserve(fn, s,
+                   {plan_of<false, false, EPI_F32>(b), plan_of<true, true, EPI_F32>(c),
+                    plan_of<true, true, EPI_F32>(d)}));
+    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, false, EPI_GELU_BWD>(fn, a, s)
+                                      : launch_gemm<false, false, EPI_SWIGLU_BWD>(fn, a, s);
+    if (st != TP_OK) return st;
+    st = run_gemm<false, false, EPI_F32>(fn, b, s);
+    if (st != TP_OK) return st;
+    st = run_gemm<true, true, EPI_F32>(fn, c, s);
+    if (st != TP_OK) return st;
+    st = run_gemm<true, true, EPI_F32>(fn, d, s);
     return st == TP_OK ? ok() : st;
 }
 
@@ -472,15 +536,14 @@ tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY, float*
     TP_TRY(check_elems(fn, k, n));
     TP_TRY(check_elems(fn, N, n));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dX_part) {
-        GemmArgs a = make_args(dY, W, dX_part, (int)N, (int)k, (int)n, (int)n, (int)n, (int)k);
-        a.accumulate = accumulate ? 1 : 0;
-        TP_TRY((launch_gemm<false, false, EPI_F32>(fn, a, s)));
-    }
-    if (dW) {
-        GemmArgs b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
-        TP_TRY((launch_gemm<true, true, EPI_F32>(fn, b, s)));
-    }
+    GemmArgs a = make_args(dY, W, dX_part, (int)N, (int)k, (int)n, (int)n, (int)n, (int)k);
+    a.accumulate = accumulate ? 1 : 0;
+    GemmArgs b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
+    TP_TRY(reserve(fn, s,
+                   {dX_part ? plan_of<false, false, EPI_F32>(a) : SplitPlan{},
+                    dW ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}}));
+    if (dX_part) TP_TRY((run_gemm<false, false, EPI_F32>(fn, a, s)));
+    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, s)));
     return ok();
 }
 
@@ -499,14 +562,13 @@ tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY, void* 
     TP_TRY(check_elems(fn, k_loc, n));
     TP_TRY(check_elems(fn, N, n));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dZ) {
-        GemmArgs a = make_args(dY, W, dZ, (int)N, (int)k_loc, (int)n, (int)n, (int)n, (int)k_loc);
-        TP_TRY((launch_gemm<false, false, EPI_BF16>(fn, a, s)));
-    }
-    if (dW) {
-        GemmArgs b = make_args(Z, dY, dW, (int)k_loc, (int)n, (int)N, (int)k_loc, (int)n, (int)n);
-        TP_TRY((launch_gemm<true, true, EPI_F32>(fn, b, s)));
-    }
+    GemmArgs a = make_args(dY, W, dZ, (int)N, (int)k_loc, (int)n, (int)n, (int)n, (int)k_loc);
+    GemmArgs b = make_args(Z, dY, dW, (int)k_loc, (int)n, (int)N, (int)k_loc, (int)n, (int)n);
+    TP_TRY(reserve(fn, s,
+                   {dZ ? plan_of<false, false, EPI_BF16>(a) : SplitPlan{},
+                    dW ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}}));
+    if (dZ) TP_TRY((run_gemm<false, false, EPI_BF16>(fn, a, s)));
+    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, s)));
     return ok();
 }
 

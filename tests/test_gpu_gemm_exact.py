@@ -75,11 +75,12 @@ def test_col_linear_nn_bf16_exact(N, k, n):
     assert torch.all(big[N * n:] == SENTINEL)
 
 
-# Decode-sized products (N <= 64) whose K is split over workgroups: ragged
-# last chunk (4160), many chunks (8192), 16 / 32 / 64-row tiles, accumulate
-# into the partial.
+# Products whose K is split over workgroups: decode sizes (N <= 64; ragged
+# last chunk, many chunks, 16 / 32 / 64-row tiles) and large products with
+# too few output tiles for the CUs (300 and 520 rows); accumulate into the
+# partial.
 SHAPES_SPLIT = [(16, 4160, 256), (40, 4160, 128), (64, 8192, 64), (3, 1024, 1280), (24, 2048, 384),
-                (16, 8192, 1280)]
+                (16, 8192, 1280), (300, 4096, 320), (520, 6208, 640)]
 
 
 @pytest.mark.parametrize("N,k,n", SHAPES_SPLIT)
@@ -110,7 +111,10 @@ def test_split_k_workspace_grows_and_shrinks():
         assert torch.all(big[N * n:] == SENTINEL)
 
 
-SHAPES_BWD = [(300, 320, 256), (16, 128, 192), (1, 64, 64), (513, 256, 128), (1000, 64, 512)]
+# (300, 320, 4096): the NT products split K = 4096; (2500, 320, 192): the TN
+# products split K = 2500 tokens (ragged last chunk)
+SHAPES_BWD = [(300, 320, 256), (16, 128, 192), (1, 64, 64), (513, 256, 128), (1000, 64, 512),
+              (300, 320, 4096), (2500, 320, 192)]
 
 
 @pytest.mark.parametrize("N,k,n", SHAPES_BWD)
@@ -144,7 +148,7 @@ def test_row_linear_bwd_exact(N, k, n):
 
 
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
-@pytest.mark.parametrize("N,h", [(1, 256), (300, 256), (16, 2048)])
+@pytest.mark.parametrize("N,h", [(1, 256), (300, 256), (16, 2048), (300, 4096)])
 def test_pre_activation_save_is_exact(act, N, h):
     # H_save is X W_in rounded once to bf16, including the SwiGLU gate/up
     # interleave (N <= 64 runs the split-K reduction's epilogue)
