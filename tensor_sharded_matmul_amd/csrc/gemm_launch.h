@@ -43,18 +43,25 @@ int device_cus();
 // shard products (a deeper ring or the full 160 KB of LDS did not help).
 template <bool A_T, bool B_KN>
 struct Rings;
-template <>
-struct Rings<false, true> {  // NN: A K-contiguous, B MN-contiguous (128 KB)
-    static constexpr int BKA = 64, SA = 2, BKB = 32, SB = 4;
+#ifndef TPS_NN_RING
+#define TPS_NN_RING 64, 2, 32, 4
+#endif
+#ifndef TPS_NT_RING
+#define TPS_NT_RING 64, 2, 64, 2
+#endif
+#ifndef TPS_TN_RING
+#define TPS_TN_RING 32, 4, 32, 3
+#endif
+template <int BKA_, int SA_, int BKB_, int SB_>
+struct RingOf {
+    static constexpr int BKA = BKA_, SA = SA_, BKB = BKB_, SB = SB_;
 };
 template <>
-struct Rings<false, false> {  // NT: both K-contiguous (128 KB)
-    static constexpr int BKA = 64, SA = 2, BKB = 64, SB = 2;
-};
+struct Rings<false, true> : RingOf<TPS_NN_RING> {};   // NN: A K-contiguous, B MN-contiguous (128 KB)
 template <>
-struct Rings<true, true> {  // TN: both MN-contiguous (112 KB)
-    static constexpr int BKA = 32, SA = 4, BKB = 32, SB = 3;
-};
+struct Rings<false, false> : RingOf<TPS_NT_RING> {};  // NT: both K-contiguous (128 KB)
+template <>
+struct Rings<true, true> : RingOf<TPS_TN_RING> {};    // TN: both MN-contiguous (106 KB)
 
 template <bool A_T, bool B_KN, int BM, int BN, int TM, int TN, int WVM, int WVN>
 using CfgOf = Cfg<BM, BN, TM, TN, Rings<A_T, B_KN>::BKA, Rings<A_T, B_KN>::SA, Rings<A_T, B_KN>::BKB,

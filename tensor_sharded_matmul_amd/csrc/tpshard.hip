@@ -148,11 +148,15 @@ static tp_status workspace(const char* fn, hipStream_t s, size_t bytes, float** 
 }
 
 // out[m][n..n+3] from the sum over splits of ws[s][m][*]. A wave covers
-// 64 / S output quads (4 columns each) with S lanes per quad, S the smallest
-// power of two >= min(ksplit, 64): lane si of a group adds splits si, si + S,
-// ..., the S partial sums are combined with butterfly shuffles, and lane 0 of
-// the group applies the epilogue. EPI_SWIGLU: ws holds [gate | up] (2 f
-// columns).
+// 64 / S output quads (4 columns each) with S lanes per quad (S a power of
+// two, chosen so that a lane has at most kReduceLoads splits to add): lane si
+// of a group loads splits si, si + S, ... (all of its loads issued before
+// the first add, so that each lane keeps several in flight), adds them in
+// that order, the S partial sums are combined with butterfly shuffles, and
+// lane 0 of the group applies the epilogue. EPI_SWIGLU: ws holds [gate | up]
+// (2 f columns).
+constexpr int kReduceLoads = 4;
+
 template <int EPI>
 __global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ ws, int ksplit, int S, int M,
                                                      int Nw, int Nout, void* C, int ldc, uint16_t* C2,
@@ -167,12 +171,23 @@ __global__ void __launch_bounds__(256) splitk_reduce(const float* __restrict__ w
     for (int64_t idx = first; idx - lane / S < total; idx += (int64_t)gridDim.x * quads_per_block) {
         const bool live = idx < total;  // every lane runs the shuffles
         const int m = live ? (int)(idx / q) : 0, n = live ? (int)(idx % q) * 4 : 0;
+        const float* row0 = ws + (size_t)m * Nw + n;
         f32x4_t v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            for (int sp = si; sp < ksplit; sp += S) {
-                const float* row = ws + sp * split_stride + (size_t)m * Nw;
-                v += *reinterpret_cast<const f32x4_t*>(row + n);
-                if constexpr (EPI == EPI_SWIGLU) u += *reinterpret_cast<const f32x4_t*>(row + f + n);
+        for (int base = 0; base < ksplit; base += kReduceLoads * S) {
+            f32x4_t tv[kReduceLoads], tu[kReduceLoads];
+#pragma unroll
+            for (int r = 0; r < kReduceLoads; ++r) {
+                const int sp = base + si + r * S;
+                const bool ok = live && sp < ksplit;
+                const float* p = row0 + (ok ? sp : 0) * split_stride;
+                tv[r] = ok ? *reinterpret_cast<const f32x4_t*>(p) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (EPI == EPI_SWIGLU)
+                    tu[r] = ok ? *reinterpret_cast<const f32x4_t*>(p + f) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int r = 0; r < kReduceLoads; ++r) {
+                v += tv[r];
+                if constexpr (EPI == EPI_SWIGLU) u += tu[r];
             }
         }
         for (int off = S / 2; off > 0; off /= 2) {
@@ -332,7 +347,7 @@ static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
         p.kper = plan.kper;
         TP_TRY((launch_gemm<A_T, B_KN, EPI_F32>(fn, p, s)));
         int S = 1;
-        while (S < plan.ksplit && S < 64) S *= 2;
+        while (S * kReduceLoads < plan.ksplit && S < 64) S *= 2;
         const long long quads = (long long)a.M * (a.N / 4);
         const long long per_block = 4 * (64 / S);
         const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
