@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (scale for HBM byte counters), then exit")
+    ap.add_argument("--regroup-only", type=int, default=0, metavar="CALLS",
+                    help="only run the fused-QKV regroup CALLS times (4 rotated sources, ranks 0..7; "
+                         "for profiling), then exit")
     return ap.parse_args()
 
 
@@ -116,6 +119,18 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {args.copy_calibration} bytes 5 times")
+        return 0
+    if args.regroup_only:
+        q = synth.WORKLOADS["llama70b_qkv_t8"]
+        width = (q.n_h + 2 * q.n_kv) * q.d_h
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(q.seed)
+        srcs = [torch.randn((q.h, width), device=dev, generator=gen).to(torch.bfloat16) for _ in range(4)]
+        dsts = [torch.empty((q.h, width // q.t), device=dev, dtype=torch.bfloat16) for _ in range(4)]
+        for i in range(args.regroup_only):
+            T.tp_qkv_regroup(srcs[i % 4], q.n_h, q.n_kv, q.d_h, q.t, (i // 4) % q.t, W_r=dsts[i % 4])
+        torch.cuda.synchronize()
+        log(f"[bench] regrouped {args.regroup_only} times")
         return 0
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")

@@ -363,29 +363,47 @@ static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Fused-QKV regroup: a bit-exact gather of three contiguous column runs per
-// row, 16 bytes per thread, output written in order (fully coalesced).
+// row. A workgroup moves kRegroupRows whole output rows as 16-byte chunks in
+// output order (coalesced writes, and reads coalesced within each run); a
+// thread issues the loads of up to kRegroupLoads chunks before their stores.
+// All index arithmetic is 32-bit within the workgroup's rows; the row base
+// is 64-bit. (2 rows x 2 loads was the fastest of 1-32 rows x 2-8 loads on
+// the Llama-3-70B t = 8 shapes: 9.3 us, against 7.0 us for a contiguous copy
+// of the same bytes; the 256-byte K and V runs of each source row cost the
+// difference.)
 // ---------------------------------------------------------------------------
+constexpr int kRegroupRows = 2, kRegroupLoads = 2;
+
 __global__ void __launch_bounds__(256) qkv_regroup_kernel(const uint16_t* __restrict__ src,
                                                           uint16_t* __restrict__ dst, int64_t h,
                                                           int src_w, int q_w, int kv_w, int q_src0,
                                                           int k_src0, int v_src0) {
     const int out_w = q_w + 2 * kv_w;
-    const int chunks_per_row = out_w >> 3;
-    const int64_t total = h * chunks_per_row;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = c / chunks_per_row;
-        const int col = (int)(c - row * chunks_per_row) << 3;
-        int scol;
-        if (col < q_w) {
-            scol = q_src0 + col;
-        } else if (col < q_w + kv_w) {
-            scol = k_src0 + (col - q_w);
-        } else {
-            scol = v_src0 + (col - q_w - kv_w);
+    const int cpr = out_w >> 3;  // 16-byte chunks per output row
+    const int64_t row0 = (int64_t)blockIdx.x * kRegroupRows;
+    const int rows = (int)min<int64_t>(kRegroupRows, h - row0);
+    const int total = rows * cpr;
+    const uint16_t* s0 = src + row0 * src_w;
+    uint16_t* d0 = dst + row0 * out_w;
+    for (int base = threadIdx.x; base < total; base += kRegroupLoads * 256) {
+        u32x4_t v[kRegroupLoads];
+        int doff[kRegroupLoads];
+#pragma unroll
+        for (int u = 0; u < kRegroupLoads; ++u) {
+            const int c = base + u * 256;
+            if (c < total) {
+                const int r = c / cpr;
+                const int col = (c - r * cpr) << 3;
+                const int scol = col < q_w ? q_src0 + col
+                                 : col < q_w + kv_w ? k_src0 + (col - q_w)
+                                                    : v_src0 + (col - q_w - kv_w);
+                v[u] = *reinterpret_cast<const u32x4_t*>(s0 + r * src_w + scol);
+                doff[u] = r * out_w + col;
+            }
         }
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + row * src_w + scol);
-        *reinterpret_cast<u32x4_t*>(dst + row * out_w + col) = v;
+#pragma unroll
+        for (int u = 0; u < kRegroupLoads; ++u)
+            if (base + u * 256 < total) *reinterpret_cast<u32x4_t*>(d0 + doff[u]) = v[u];
     }
 }
 
@@ -616,9 +634,9 @@ tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h, int32_t n_h, i
     const int q_src0 = rank * q_w;
     const int k_src0 = n_h * d_h + rank * kv_w;
     const int v_src0 = (n_h + n_kv) * d_h + rank * kv_w;
-    const int64_t chunks = h * ((q_w + 2 * kv_w) / 8);
-    int64_t blocks = (chunks + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    const int64_t blocks = (h + kRegroupRows - 1) / kRegroupRows;
+    if (blocks > 0x7fffffffLL || (int64_t)kRegroupRows * src_w > 0x7fffffffLL)
+        return fail(TP_ERR_UNSUPPORTED, "%s: h or the fused width is too large", fn);
     hipLaunchKernelGGL(qkv_regroup_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W_qkv),
                        static_cast<uint16_t*>(W_r), h, src_w, q_w, kv_w, q_src0, k_src0, v_src0);
