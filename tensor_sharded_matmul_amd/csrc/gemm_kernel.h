@@ -326,8 +326,73 @@ __device__ __forceinline__ void unpack4(u32x2_t v, float (&x)[4]) {
     x[3] = bf16_bits_to_f32(v[1] >> 16);
 }
 
+// Activation-backward epilogues (GeLU', SwiGLU'): dZ in the accumulators,
+// the saved pre-activation H read from memory. H of row block i + 1 is
+// loaded before row block i is computed and stored, so that its latency
+// overlaps the math (two row blocks of H in registers).
+template <int MI, int NI, int EPI>
+__device__ __forceinline__ void epilogue_act_bwd(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,
+                                                 int nb) {
+    constexpr int NH = EPI == EPI_SWIGLU_BWD ? 2 : 1;  // H columns read per output column: g (and u)
+    u32x2_t hb[2][NI][NH];
+    auto load_rows = [&](auto ic) {
+        constexpr int i = decltype(ic)::value, buf = i % 2;
+        const int m = mb + i * 16;
+        const uint16_t* hrow = args.aux + (size_t)m * args.ldc2;
+        static_for<0, NI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int n = nb + j * 16;
+            if (m < args.M && n < args.N) {
+                hb[buf][j][0] = *reinterpret_cast<const u32x2_t*>(hrow + n);
+                if constexpr (NH == 2) hb[buf][j][1] = *reinterpret_cast<const u32x2_t*>(hrow + args.f + n);
+            }
+        });
+    };
+    load_rows(std::integral_constant<int, 0>{});
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, buf = i % 2;
+        if constexpr (i + 1 < MI) load_rows(std::integral_constant<int, i + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        const int m = mb + i * 16;
+        if (m < args.M) {
+            uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
+            static_for<0, NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int n = nb + j * 16;
+                if (n < args.N) {
+                    const f32x4_t dz = acc[i][j];
+                    if constexpr (EPI == EPI_GELU_BWD) {
+                        float x[4];
+                        unpack4(hb[buf][j][0], x);
+                        *reinterpret_cast<u32x2_t*>(crow + n) =
+                            pack4(dz[0] * gelu_grad_f(x[0]), dz[1] * gelu_grad_f(x[1]),
+                                  dz[2] * gelu_grad_f(x[2]), dz[3] * gelu_grad_f(x[3]));
+                    } else {
+                        float g[4], u[4], dg[4], du[4];
+                        unpack4(hb[buf][j][0], g);
+                        unpack4(hb[buf][j][1], u);
+                        static_for<0, 4>([&](auto rc) {
+                            constexpr int r = decltype(rc)::value;
+                            const float sg = sigmoid_f(g[r]);
+                            du[r] = dz[r] * g[r] * sg;
+                            dg[r] = dz[r] * u[r] * (sg + g[r] * sg * (1.0f - sg));
+                        });
+                        *reinterpret_cast<u32x2_t*>(crow + n) = pack4(dg[0], dg[1], dg[2], dg[3]);
+                        *reinterpret_cast<u32x2_t*>(crow + args.f + n) = pack4(du[0], du[1], du[2], du[3]);
+                    }
+                }
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 template <int MI, int NI, int EPI>
 __device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb, int nb) {
+    if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) {
+        epilogue_act_bwd<MI, NI, EPI>(acc, args, mb, nb);
+        return;
+    }
     static_for<0, MI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const int m = mb + i * 16;
@@ -381,35 +446,6 @@ __device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const Gem
                             uint16_t* hrow = args.C2 + (size_t)m * args.ldc2;
                             *reinterpret_cast<u32x2_t*>(hrow + n) = pack4(g[0], g[1], g[2], g[3]);
                             *reinterpret_cast<u32x2_t*>(hrow + args.f + n) = pack4(u[0], u[1], u[2], u[3]);
-                        }
-                    }
-                });
-            } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) {
-                uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
-                const uint16_t* hrow = args.aux + (size_t)m * args.ldc2;
-                static_for<0, NI>([&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    const int n = nb + j * 16;
-                    if (n < args.N) {
-                        const f32x4_t dz = acc[i][j];
-                        if constexpr (EPI == EPI_GELU_BWD) {
-                            float x[4];
-                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + n), x);
-                            *reinterpret_cast<u32x2_t*>(crow + n) =
-                                pack4(dz[0] * gelu_grad_f(x[0]), dz[1] * gelu_grad_f(x[1]),
-                                      dz[2] * gelu_grad_f(x[2]), dz[3] * gelu_grad_f(x[3]));
-                        } else {
-                            float g[4], u[4], dg[4], du[4];
-                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + n), g);
-                            unpack4(*reinterpret_cast<const u32x2_t*>(hrow + args.f + n), u);
-                            static_for<0, 4>([&](auto rc) {
-                                constexpr int r = decltype(rc)::value;
-                                const float sg = sigmoid_f(g[r]);
-                                du[r] = dz[r] * g[r] * sg;
-                                dg[r] = dz[r] * u[r] * (sg + g[r] * sg * (1.0f - sg));
-                            });
-                            *reinterpret_cast<u32x2_t*>(crow + n) = pack4(dg[0], dg[1], dg[2], dg[3]);
-                            *reinterpret_cast<u32x2_t*>(crow + args.f + n) = pack4(du[0], du[1], du[2], du[3]);
                         }
                     }
                 });
