@@ -17,6 +17,7 @@ __all__ = [
     "mlp_shard_bwd", "mlp_shard_fwd_rows", "mlp_shard_bwd_rows",
     "mlp_shard_bwd_cols", "col_linear_bwd", "row_linear_bwd",
     "qkv_regroup_index", "qkv_regroup", "naive_split_index", "shard_shape",
+    "kv_heads_of_rank", "kv_replica_ranks", "kv_grad_accumulate", "kv_replica_grad_sum",
     "ShardError", "llama_layer_params", "llama_model_params",
     "llama_shard_weight_shapes", "gemm_flops", "mlp_shard_flops",
     "check_heads_divisible", "rel_err",
@@ -245,16 +246,32 @@ def mlp_shard_bwd_cols(X, W_in, W_out, dY, act, cols):
 # ---------------------------------------------------------------------------
 
 def check_heads_divisible(n_h, n_kv, t):
-    """Head-count rules: t <= n_h and t | n_h ([TPSP]; [REVISIT] Megatron's
-    ValueError); the clean GQA case needs t <= n_kv and t | n_kv."""
+    """Head-count rules ([TPSP] "注意力：按头切，以及 GQA 的约束" and "GQA：KV 头比
+    query 头少"; [REVISIT] Megatron's ValueError): heads are the unit of the
+    split, so t <= n_h and t | n_h. With t <= n_kv each rank takes n_kv / t
+    whole KV heads (t | n_kv); with n_kv < t every KV head is replicated on
+    t / n_kv ranks, which needs n_kv | t."""
     if t <= 0:
         raise ValueError("TP degree must be positive")
     if n_h % t != 0:
         raise ValueError(f"num_attention_heads ({n_h}) must be a multiple of "
                          f"tensor_model_parallel_size ({t}).")
-    if n_kv % t != 0:
+    if t <= n_kv and n_kv % t != 0:
         raise ValueError(f"num_kv_heads ({n_kv}) must be a multiple of "
-                         f"tensor_model_parallel_size ({t}) (KV-head replication not handled).")
+                         f"tensor_model_parallel_size ({t}).")
+    if t > n_kv and t % n_kv != 0:
+        raise ValueError(f"tensor_model_parallel_size ({t}) must be a multiple of "
+                         f"num_kv_heads ({n_kv}) to replicate KV heads.")
+
+
+def kv_heads_of_rank(n_kv, t, rank):
+    """KV heads held by ``rank``: [r n_kv/t, (r+1) n_kv/t) when t <= n_kv;
+    with n_kv < t the single head r // (t / n_kv), which the rank's query heads
+    [r n_h/t, (r+1) n_h/t) all use (contiguous grouping: query head j uses KV
+    head j // (n_h / n_kv))."""
+    if t <= n_kv:
+        return list(range(rank * (n_kv // t), (rank + 1) * (n_kv // t)))
+    return [rank // (t // n_kv)]
 
 
 def qkv_regroup_index(n_h, n_kv, d_h, t, rank):
@@ -263,22 +280,24 @@ def qkv_regroup_index(n_h, n_kv, d_h, t, rank):
     Source layout [h, (n_h + 2 n_kv) d_h] = [Q heads 0..n_h-1 | K heads
     0..n_kv-1 | V heads 0..n_kv-1], each head's d_h columns contiguous. The
     rank's slice holds, in order, its own query heads, its own K heads and its
-    own V heads: query heads [r n_h/t, (r+1) n_h/t) and KV heads
-    [r n_kv/t, (r+1) n_kv/t), so each query group sits with the KV head it
-    shares (contiguous GQA grouping: query head j uses KV head j // (n_h/n_kv)).
+    own V heads ([TPSP] "几个实现细节", fused-QKV layout): query heads
+    [r n_h/t, (r+1) n_h/t) and the KV heads of kv_heads_of_rank, so each query
+    group sits with the KV head it shares. With n_kv < t the KV head is a
+    replica, present on t / n_kv ranks ([TPSP] "GQA：KV 头比 query 头少").
     """
     check_heads_divisible(n_h, n_kv, t)
     if not 0 <= rank < t:
         raise ValueError(f"rank {rank} out of range for TP degree {t}")
-    qh, kvh = n_h // t, n_kv // t
+    qh = n_h // t
+    kv = kv_heads_of_rank(n_kv, t, rank)
     idx = []
     for head in range(rank * qh, (rank + 1) * qh):            # own Q heads
         idx.extend(range(head * d_h, (head + 1) * d_h))
     k_base = n_h * d_h
-    for head in range(rank * kvh, (rank + 1) * kvh):          # own K heads
+    for head in kv:                                           # own K heads
         idx.extend(range(k_base + head * d_h, k_base + (head + 1) * d_h))
     v_base = (n_h + n_kv) * d_h
-    for head in range(rank * kvh, (rank + 1) * kvh):          # own V heads
+    for head in kv:                                           # own V heads
         idx.extend(range(v_base + head * d_h, v_base + (head + 1) * d_h))
     return np.array(idx, dtype=np.int64)
 
@@ -286,6 +305,42 @@ def qkv_regroup_index(n_h, n_kv, d_h, t, rank):
 def qkv_regroup(W_qkv, n_h, n_kv, d_h, t, rank):
     """W_r = W_qkv[:, qkv_regroup_index(...)] (exact copy of bf16 bit patterns)."""
     return np.ascontiguousarray(np.asarray(W_qkv)[:, qkv_regroup_index(n_h, n_kv, d_h, t, rank)])
+
+
+def kv_replica_ranks(n_kv, t, head):
+    """Ranks holding a replica of KV head ``head`` when n_kv < t."""
+    r = t // n_kv
+    return list(range(head * r, (head + 1) * r))
+
+
+def kv_grad_accumulate(dst, src, n_h, n_kv, d_h, t):
+    """One step of the replica-gradient sum ([TPSP] "GQA：KV 头比 query 头少": the
+    replicas' K/V weight gradients are different partial sums). ``dst`` and
+    ``src`` are two replica ranks' weight-gradient shards [h, (n_h/t + 2) d_h]
+    laid out like their W_r; returns dst with its K|V columns (the last 2 d_h)
+    plus src's. The Q columns belong to each rank alone and are kept."""
+    check_heads_divisible(n_h, n_kv, t)
+    if not n_kv < t:
+        raise ValueError("KV heads are replicated only when n_kv < t")
+    out = np.array(dst, dtype=np.float64, copy=True)
+    q = (n_h // t) * d_h
+    out[:, q:] += np.asarray(src, dtype=np.float64)[:, q:]
+    return out
+
+
+def kv_replica_grad_sum(dWs, n_h, n_kv, d_h, t):
+    """The synchronised K|V gradient of every KV head: for head g, the sum in
+    rank order of the K|V columns of the weight-gradient shards of the ranks
+    in kv_replica_ranks(g). ``dWs``: the t shards. Returns {g: [h, 2 d_h]}."""
+    q = (n_h // t) * d_h
+    out = {}
+    for g in range(n_kv):
+        acc = None
+        for r in kv_replica_ranks(n_kv, t, g):
+            part = np.asarray(dWs[r], dtype=np.float64)[:, q:]
+            acc = part.copy() if acc is None else acc + part
+        out[g] = acc
+    return out
 
 
 def naive_split_index(n_h, n_kv, d_h, t, rank):

@@ -72,9 +72,83 @@ def test_regroup_divisibility_errors():
     with pytest.raises(ValueError, match="must be a multiple of"):
         O.qkv_regroup_index(64, 8, 128, 7, 0)
     with pytest.raises(ValueError):
-        O.qkv_regroup_index(64, 8, 128, 16, 0)    # n_kv < t: replication not handled
+        O.qkv_regroup_index(48, 8, 128, 12, 0)    # n_kv < t but KV heads cannot be replicated evenly
+    with pytest.raises(ValueError):
+        O.qkv_regroup_index(32, 8, 128, 64, 0)    # more ranks than query heads
     with pytest.raises(ValueError):
         O.qkv_regroup_index(64, 8, 128, 8, 8)
+
+
+@pytest.mark.parametrize("t", [16, 32])
+def test_replicated_kv_heads_llama3_8b(t):
+    # [TPSP] "GQA：KV 头比 query 头少": Llama-3 8B has 32 query and 8 KV heads; TP can
+    # go to 32, and past 8 every KV head is copied to t / 8 cards, each serving its
+    # own query heads with it
+    n_h, n_kv, d_h = 32, 8, 128
+    qh, group = n_h // t, n_h // n_kv
+    q_cols, kv_count = [], np.zeros(2 * n_kv, dtype=int)
+    for r in range(t):
+        idx = O.qkv_regroup_index(n_h, n_kv, d_h, t, r)
+        assert idx.shape == ((qh + 2) * d_h,)
+        q, k, v = idx[: qh * d_h], idx[qh * d_h: (qh + 1) * d_h], idx[(qh + 1) * d_h:]
+        q_cols.append(q)
+        kh = (int(k[0]) - n_h * d_h) // d_h
+        vh = (int(v[0]) - (n_h + n_kv) * d_h) // d_h
+        assert kh == vh == r // (t // n_kv)
+        assert np.array_equal(k, n_h * d_h + kh * d_h + np.arange(d_h))
+        assert np.array_equal(v, (n_h + n_kv) * d_h + vh * d_h + np.arange(d_h))
+        # every query head on this rank uses the KV head on this rank
+        assert all(int(c) // d_h // group == kh for c in q)
+        kv_count[kh] += 1
+        kv_count[n_kv + vh] += 1
+        assert r in O.kv_replica_ranks(n_kv, t, kh)
+    assert np.array_equal(np.sort(np.concatenate(q_cols)), np.arange(n_h * d_h))
+    assert np.all(kv_count == t // n_kv)
+
+
+def test_replica_kv_gradients_sum_to_the_full_gradient():
+    # With replicated KV heads each replica's K/V weight gradient is a partial
+    # sum ([TPSP] "GQA：KV 头比 query 头少"). Loss L = sum_r <G_r, X W_qkv[:, idx_r]>
+    # (rank r's projection with upstream gradient G_r); its gradient with respect
+    # to W_qkv, by central differences, must equal each rank's own Q columns of
+    # X^T G_r and, for each KV head, the replicas' K|V columns summed.
+    rng = np.random.default_rng(11)
+    n_h, n_kv, d_h, t, h, N = 4, 2, 2, 4, 3, 5
+    width = (n_h + 2 * n_kv) * d_h
+    X = rng.standard_normal((N, h))
+    W = rng.standard_normal((h, width))
+    idxs = [O.qkv_regroup_index(n_h, n_kv, d_h, t, r) for r in range(t)]
+    G = [rng.standard_normal((N, len(i))) for i in idxs]
+
+    def loss(Wq):
+        return sum(float(np.sum(G[r] * (X @ Wq[:, idxs[r]]))) for r in range(t))
+
+    fd = np.zeros_like(W)
+    eps = 1e-3
+    for a in range(h):
+        for b in range(width):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[a, b] += eps
+            Wm[a, b] -= eps
+            fd[a, b] = (loss(Wp) - loss(Wm)) / (2 * eps)
+    dWs = [O.col_linear_bwd(X, W[:, idxs[r]], G[r])[1] for r in range(t)]
+    qw = (n_h // t) * d_h
+    for r in range(t):
+        assert np.allclose(dWs[r][:, :qw], fd[:, idxs[r][:qw]], atol=1e-8)
+    sums = O.kv_replica_grad_sum(dWs, n_h, n_kv, d_h, t)
+    for g in range(n_kv):
+        k_cols = n_h * d_h + g * d_h + np.arange(d_h)
+        v_cols = (n_h + n_kv) * d_h + g * d_h + np.arange(d_h)
+        assert np.allclose(sums[g], fd[:, np.concatenate([k_cols, v_cols])], atol=1e-8)
+        # the pairwise accumulate, in rank order, gives the same sum; Q untouched
+        ranks = O.kv_replica_ranks(n_kv, t, g)
+        acc = dWs[ranks[0]]
+        for r in ranks[1:]:
+            acc = O.kv_grad_accumulate(acc, dWs[r], n_h, n_kv, d_h, t)
+        assert np.array_equal(acc[:, qw:], sums[g])
+        assert np.array_equal(acc[:, :qw], dWs[ranks[0]][:, :qw])
+    with pytest.raises(ValueError):
+        O.kv_grad_accumulate(dWs[0], dWs[1], 8, 8, 2, 4)       # no replicas when t <= n_kv
 
 
 def test_shard_shape_pop_quiz():
