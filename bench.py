@@ -342,7 +342,37 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     res["qkv_regroup"] = {"ms": round(ms, 5), "ms_eager": round(ms_eager, 5), "bytes": moved,
                           "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
                           "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
-    del srcs, dsts
+    # the same at t = 16 > n_kv = 8: each KV head replicated on two ranks
+    t16 = 16
+    w16 = T.regroup_width(n_h, n_kv, d_h, t16)
+    dsts = [torch.empty((h, w16), device=dev, dtype=bf) for _ in range(4)]
+    it[0] = 0
+
+    def regroup16():
+        i = it[0]
+        it[0] += 1
+        T.tp_qkv_regroup(srcs[i % 4], n_h, n_kv, d_h, t16, (i // 4) % t16, W_r=dsts[i % 4])
+
+    ms = time_graph(regroup16, 32)
+    moved = 2 * h * w16 * 2
+    res["qkv_regroup_t16_replicated_kv"] = {"ms": round(ms, 5), "bytes": moved,
+                                            "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                                            "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    # replica K|V weight-gradient sum at t = 16 (f32 [h, (n_h/t + 2) d_h] shards)
+    gw = [torch.randn((h, w16), device=dev, generator=gen) for _ in range(8)]
+    it[0] = 0
+
+    def kv_sum():
+        i = it[0]
+        it[0] += 1
+        T.tp_kv_grad_accumulate(gw[(2 * i) % 8], gw[(2 * i + 1) % 8], n_h, n_kv, d_h, t16)
+
+    ms = time_graph(kv_sum, 32)
+    moved = 3 * h * 2 * d_h * 4
+    res["kv_grad_accumulate_t16"] = {"ms": round(ms, 5), "bytes": moved,
+                                     "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    del srcs, dsts, gw
 
     # --- attention projections: QKV column GEMM + W_O row partial, fwd and bwd ---
     dq = synth.qkv_inputs(q.seed, q.N, h, n_h, n_kv, d_h, t)

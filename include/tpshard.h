@@ -180,20 +180,41 @@ tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY,
 /*
  * Per-rank regroup of the fused QKV weight ([TPSP] attention section, fused
  * QKV item: an equal column split is wrong; each rank's slice must hold its
- * own Q heads, then its own K heads, then its own V heads; "GQA" section:
- * t | n_kv keeps each query group with its KV head).
+ * own Q heads, then its own K heads, then its own V heads; "GQA：KV 头比 query
+ * 头少": a query group stays with the KV head it shares).
  *   W_qkv bf16 [h, (n_h + 2 n_kv) d_h] = [Q heads 0..n_h-1 | K heads 0..n_kv-1
  *         | V heads 0..n_kv-1], each head's d_h columns contiguous.
- *   W_r   bf16 [h, (n_h + 2 n_kv) d_h / t] = [Q heads r n_h/t .. (r+1) n_h/t - 1
- *         | K heads r n_kv/t .. | V heads r n_kv/t ..].
+ *   W_r   bf16 [h, (n_h/t + 2 c) d_h] = [Q heads r n_h/t .. (r+1) n_h/t - 1
+ *         | c K heads | the same c V heads], where
+ *         t <= n_kv: c = n_kv/t, KV heads r n_kv/t .. (r+1) n_kv/t - 1;
+ *         n_kv < t:  c = 1, KV head r / (t/n_kv), replicated on the t/n_kv
+ *                    ranks whose query heads use it.
  * A bit-exact copy. Errors: NOT_DIVISIBLE when t does not divide n_h
- * (message in Megatron's wording, [REVISIT]); UNSUPPORTED when t does not
- * divide n_kv (KV-head replication for n_kv < t is not implemented);
- * INVALID_ARG for rank outside [0, t), d_h not a multiple of 8, bad pointers.
+ * (message in Megatron's wording, [REVISIT]), when t <= n_kv and t does not
+ * divide n_kv, or when n_kv < t and n_kv does not divide t; INVALID_ARG for
+ * rank outside [0, t), d_h not a multiple of 8, bad pointers.
  */
 tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h,
                          int32_t n_h, int32_t n_kv, int32_t d_h,
                          int32_t t, int32_t rank, void* stream);
+
+/*
+ * Replicated KV heads, backward ([TPSP] "GQA：KV 头比 query 头少": with n_kv < t
+ * each KV head sits on t/n_kv ranks, and their K/V weight gradients are
+ * different partial sums that an extra exchange must sum). The single-device
+ * stand-in for that exchange: called once per further replica, in rank
+ * order, it adds the K|V columns of one replica rank's weight-gradient shard
+ * into another's.
+ *   dW_dst, dW_src f32 [h, (n_h/t + 2) d_h], laid out like the ranks' W_r
+ *   (tp_col_linear_bwd's dW of the QKV projection);
+ *   dW_dst[:, (n_h/t) d_h :] += dW_src[:, (n_h/t) d_h :]; the Q columns of
+ *   dW_dst are left as they are.
+ * Errors: INVALID_ARG unless n_kv < t (no replicas otherwise), for d_h not a
+ * multiple of 4 or bad pointers; NOT_DIVISIBLE as for tp_qkv_regroup.
+ */
+tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h,
+                                int32_t n_h, int32_t n_kv, int32_t d_h,
+                                int32_t t, void* stream);
 
 /*
  * Shard arithmetic of a tensor over a device mesh ([SB6] §6.1): host only,

@@ -62,6 +62,7 @@ def load():
         "tp_col_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp], ctypes.c_int),
         "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
         "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
+        "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], ctypes.c_int),
         "tp_shard_shape": ([i32, ctypes.POINTER(i64), i32, i32, ctypes.POINTER(i64),
                             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64),
                             ctypes.POINTER(i64), ctypes.POINTER(i64)], ctypes.c_int),
@@ -241,6 +242,15 @@ def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, st
     return (dZ if want_dz else None), (dW if want_dw else None)
 
 
+def regroup_width(n_h, n_kv, d_h, t):
+    """Columns of one rank's W_r: its n_h/t query heads plus n_kv/t K and V heads
+    (one replicated K and V head when n_kv < t); 0 for an invalid t."""
+    if t <= 0 or n_h % t:
+        return 0
+    kv = n_kv // t if t <= n_kv else 1
+    return (n_h // t + 2 * kv) * d_h
+
+
 def tp_qkv_regroup(W_qkv, n_h, n_kv, d_h, t, rank, W_r=None, stream=None):
     """Rank-local [Q_r | K_r | V_r] columns of the fused QKV weight; returns W_r."""
     lib = load()
@@ -248,13 +258,25 @@ def tp_qkv_regroup(W_qkv, n_h, n_kv, d_h, t, rank, W_r=None, stream=None):
     if width != (n_h + 2 * n_kv) * d_h:
         raise ValueError(f"W_qkv width {width} != (n_h + 2 n_kv) d_h = {(n_h + 2 * n_kv) * d_h}")
     _dev(W_qkv, "W_qkv", _bf16, (h, width))
-    out_w = width // t if t > 0 and width % t == 0 else 0
+    out_w = regroup_width(n_h, n_kv, d_h, t)
     if W_r is None:
         W_r = torch.empty((h, out_w), dtype=_bf16, device=W_qkv.device)
     else:
         _dev(W_r, "W_r", _bf16, (h, out_w))
     _check(lib.tp_qkv_regroup(_ptr(W_qkv), _ptr(W_r), h, n_h, n_kv, d_h, t, rank, _stream(stream)))
     return W_r
+
+
+def tp_kv_grad_accumulate(dW_dst, dW_src, n_h, n_kv, d_h, t, stream=None):
+    """dW_dst[:, K|V columns] += dW_src[:, K|V columns] for two replica ranks'
+    weight-gradient shards (n_kv < t); returns dW_dst."""
+    lib = load()
+    h = dW_dst.shape[0]
+    w = (n_h // t + 2) * d_h if t > 0 else 0
+    _dev(dW_dst, "dW_dst", _f32, (h, w))
+    _dev(dW_src, "dW_src", _f32, (h, w))
+    _check(lib.tp_kv_grad_accumulate(_ptr(dW_dst), _ptr(dW_src), h, n_h, n_kv, d_h, t, _stream(stream)))
+    return dW_dst
 
 
 def tp_shard_shape(shape, elem_bytes, axis_sizes, dim_axis_mask):

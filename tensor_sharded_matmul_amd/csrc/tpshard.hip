@@ -361,6 +361,37 @@ static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
     }
 }
 
+// KV-head rules of the QKV split: t | n_kv (each rank takes n_kv / t heads),
+// or n_kv < t with n_kv | t (each head replicated on t / n_kv ranks).
+static tp_status check_kv_heads(const char* fn, int n_kv, int t) {
+    if (t <= n_kv && n_kv % t != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE,
+                    "%s: num_kv_heads (%d) must be a multiple of tensor_model_parallel_size (%d).", fn, n_kv,
+                    t);
+    if (t > n_kv && t % n_kv != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE,
+                    "%s: tensor_model_parallel_size (%d) must be a multiple of num_kv_heads (%d) to "
+                    "replicate KV heads.",
+                    fn, t, n_kv);
+    return TP_OK;
+}
+
+// dst[row][c0 + c] += src[row][c0 + c] for c in [0, w): one thread per 4
+// columns, rows of width ld (f32).
+__global__ void __launch_bounds__(256) kv_grad_accumulate_kernel(float* __restrict__ dst,
+                                                                 const float* __restrict__ src, int64_t h,
+                                                                 int ld, int c0, int w) {
+    const int q = w >> 2;
+    const int64_t total = h * q;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / q;
+        const int c = c0 + (int)(i - row * q) * 4;
+        f32x4_t* d = reinterpret_cast<f32x4_t*>(dst + row * ld + c);
+        *d = *d + *reinterpret_cast<const f32x4_t*>(src + row * ld + c);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Fused-QKV regroup: a bit-exact gather of three contiguous column runs per
 // row. A workgroup moves kRegroupRows whole output rows as 16-byte chunks in
@@ -615,11 +646,7 @@ tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h, int32_t n_h, i
         return fail(TP_ERR_NOT_DIVISIBLE,
                     "%s: num_attention_heads (%d) must be a multiple of tensor_model_parallel_size (%d).",
                     fn, n_h, t);
-    if (n_kv % t != 0)
-        return fail(TP_ERR_UNSUPPORTED,
-                    "%s: num_kv_heads (%d) is not a multiple of the TP degree (%d); KV-head replication "
-                    "is not implemented",
-                    fn, n_kv, t);
+    TP_TRY(check_kv_heads(fn, n_kv, t));
     if (rank < 0 || rank >= t) return fail(TP_ERR_INVALID_ARG, "%s: rank %d outside [0, %d)", fn, rank, t);
     if (d_h % 8 != 0) return fail(TP_ERR_INVALID_ARG, "%s: d_h = %d must be a multiple of 8", fn, d_h);
     if (h < 0) return fail(TP_ERR_INVALID_ARG, "%s: h = %lld < 0", fn, (long long)h);
@@ -628,18 +655,54 @@ tp_status tp_qkv_regroup(const void* W_qkv, void* W_r, int64_t h, int32_t n_h, i
     if (h == 0) return ok();
     TP_CHECK_PTR(W_qkv, "W_qkv");
     TP_CHECK_PTR(W_r, "W_r");
+    // t <= n_kv: KV heads [r n_kv/t, (r+1) n_kv/t); n_kv < t: the one head
+    // r / (t / n_kv), replicated on t / n_kv ranks
     const int q_w = n_h / t * d_h;
-    const int kv_w = n_kv / t * d_h;
+    const int kv_heads = t <= n_kv ? n_kv / t : 1;
+    const int kv_first = t <= n_kv ? rank * (n_kv / t) : rank / (t / n_kv);
+    const int kv_w = kv_heads * d_h;
     const int src_w = (int)src_w64;
     const int q_src0 = rank * q_w;
-    const int k_src0 = n_h * d_h + rank * kv_w;
-    const int v_src0 = (n_h + n_kv) * d_h + rank * kv_w;
+    const int k_src0 = n_h * d_h + kv_first * d_h;
+    const int v_src0 = (n_h + n_kv) * d_h + kv_first * d_h;
     const int64_t blocks = (h + kRegroupRows - 1) / kRegroupRows;
     if (blocks > 0x7fffffffLL || (int64_t)kRegroupRows * src_w > 0x7fffffffLL)
         return fail(TP_ERR_UNSUPPORTED, "%s: h or the fused width is too large", fn);
     hipLaunchKernelGGL(qkv_regroup_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(W_qkv),
                        static_cast<uint16_t*>(W_r), h, src_w, q_w, kv_w, q_src0, k_src0, v_src0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h, int32_t n_h, int32_t n_kv,
+                                int32_t d_h, int32_t t, void* stream) {
+    const char* fn = "tp_kv_grad_accumulate";
+    if (t <= 0) return fail(TP_ERR_INVALID_ARG, "%s: TP degree t = %d must be positive", fn, t);
+    if (n_h <= 0 || n_kv <= 0 || d_h <= 0)
+        return fail(TP_ERR_INVALID_ARG, "%s: head counts and head width must be positive", fn);
+    if (n_h % t != 0)
+        return fail(TP_ERR_NOT_DIVISIBLE,
+                    "%s: num_attention_heads (%d) must be a multiple of tensor_model_parallel_size (%d).",
+                    fn, n_h, t);
+    TP_TRY(check_kv_heads(fn, n_kv, t));
+    if (t <= n_kv)
+        return fail(TP_ERR_INVALID_ARG, "%s: KV heads are replicated only when n_kv (%d) < t (%d)", fn, n_kv,
+                    t);
+    if (d_h % 4 != 0) return fail(TP_ERR_INVALID_ARG, "%s: d_h = %d must be a multiple of 4", fn, d_h);
+    if (h < 0) return fail(TP_ERR_INVALID_ARG, "%s: h = %lld < 0", fn, (long long)h);
+    const int64_t ld = (int64_t)(n_h / t + 2) * d_h;
+    if (ld > 0x7fffffff) return fail(TP_ERR_UNSUPPORTED, "%s: shard width too large", fn);
+    TP_TRY(check_elems(fn, h, ld));
+    if (h == 0) return ok();
+    TP_CHECK_PTR(dW_dst, "dW_dst");
+    TP_CHECK_PTR(dW_src, "dW_src");
+    const int c0 = n_h / t * d_h, w = 2 * d_h;
+    const int64_t work = h * (w / 4);
+    const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 8192);
+    hipLaunchKernelGGL(kv_grad_accumulate_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       dW_dst, dW_src, h, (int)ld, c0, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

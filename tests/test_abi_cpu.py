@@ -82,12 +82,29 @@ def test_regroup_divisibility_errors_before_launch():
     f = _raw("tp_qkv_regroup")
     assert f(NULL, NULL, 8192, 64, 8, 128, 7, 0, NULL) == 2          # NOT_DIVISIBLE
     assert "must be a multiple of tensor_model_parallel_size" in T.tp_last_error()
-    assert f(NULL, NULL, 8192, 64, 8, 128, 16, 0, NULL) == 3         # n_kv < t: unsupported
+    assert f(NULL, NULL, 8192, 48, 8, 128, 12, 0, NULL) == 2         # n_kv < t, n_kv does not divide t
+    assert "replicate KV heads" in T.tp_last_error()
+    assert f(NULL, NULL, 8192, 64, 8, 128, 16, 0, NULL) == 1         # replicated KV heads: valid, NULL W_qkv
     assert f(NULL, NULL, 8192, 64, 8, 128, 8, 8, NULL) == 1          # rank out of range
     assert f(NULL, NULL, 8192, 64, 8, 12, 8, 0, NULL) == 1           # d_h % 8
     assert f(NULL, NULL, 8192, 64, 8, 128, 8, 0, NULL) == 1          # NULL pointers
     assert "NULL" in T.tp_last_error()
     assert f(NULL, NULL, 0, 64, 8, 128, 8, 0, NULL) == 0             # h = 0: nothing to do
+
+
+def test_kv_grad_accumulate_validates_before_launch():
+    f = _raw("tp_kv_grad_accumulate")
+    assert f(NULL, NULL, 8192, 64, 8, 128, 8, NULL) == 1             # t <= n_kv: no replicas
+    assert "replicated only" in T.tp_last_error()
+    assert f(NULL, NULL, 8192, 48, 8, 128, 12, NULL) == 2            # 8 does not divide 12
+    assert f(NULL, NULL, 8192, 64, 8, 126, 16, NULL) == 1            # d_h % 4
+    assert f(NULL, NULL, 8192, 64, 8, 128, 16, NULL) == 1            # NULL pointers
+    assert f(NULL, NULL, 0, 64, 8, 128, 16, NULL) == 0               # h = 0: nothing to do
+
+
+def test_regroup_width_matches_oracle():
+    for n_h, n_kv, d_h, t in [(64, 8, 128, 8), (64, 8, 128, 16), (32, 8, 128, 32), (64, 8, 128, 4)]:
+        assert T.regroup_width(n_h, n_kv, d_h, t) == len(O.qkv_regroup_index(n_h, n_kv, d_h, t, 0))
 
 
 def test_gemm_entry_points_validate_before_launch():
