@@ -18,6 +18,7 @@ __all__ = [
     "mlp_shard_bwd_cols", "col_linear_bwd", "row_linear_bwd",
     "qkv_regroup_index", "qkv_regroup", "naive_split_index", "shard_shape",
     "kv_heads_of_rank", "kv_replica_ranks", "kv_grad_accumulate", "kv_replica_grad_sum",
+    "vocab_ce_local", "vocab_ce_loss", "vocab_ce_bwd",
     "ShardError", "llama_layer_params", "llama_model_params",
     "llama_shard_weight_shapes", "gemm_flops", "mlp_shard_flops",
     "check_heads_divisible", "rel_err",
@@ -348,6 +349,64 @@ def naive_split_index(n_h, n_kv, d_h, t, rank):
     width = (n_h + 2 * n_kv) * d_h
     w = width // t
     return np.arange(rank * w, (rank + 1) * w, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Vocab-parallel LM head with cross-entropy ([TPSP] "词表并行：embedding 与交叉熵",
+# "LM head 与交叉熵"): W_out [h, V] split by columns (vocab), rank i holding
+# vocab ids [i V/t, (i+1) V/t); the logits z^(i) = X W_i are never gathered.
+# ---------------------------------------------------------------------------
+
+def vocab_ce_local(X, W_i, targets, vocab_start):
+    """Rank i's local part of the fused cross-entropy: its logits z = X W_i
+    [N, V/t]; per token the local maximum m_i, the local sum
+    s_i = sum_v exp(z_v - m_i) over its vocab range, and the target logit z_y
+    when the target id falls in [vocab_start, vocab_start + V/t) (0 otherwise:
+    the target lands on exactly one rank)."""
+    z = np.asarray(X, np.float64) @ np.asarray(W_i, np.float64)
+    y = np.asarray(targets, np.int64) - vocab_start
+    m = z.max(axis=1)
+    s = np.exp(z - m[:, None]).sum(axis=1)
+    inside = (y >= 0) & (y < z.shape[1])
+    zy = np.where(inside, z[np.arange(z.shape[0]), np.clip(y, 0, z.shape[1] - 1)], 0.0)
+    return m, s, zy
+
+
+def vocab_ce_loss(X, W_shards, targets):
+    """The page's four steps over t vocab shards, each over the shard's own
+    logits: (1) the global max m of the local maxima (All-Reduce MAX);
+    (2) S = sum over shards of sum_v exp(z_v - m) (All-Reduce SUM); (3) z_y
+    from the one shard that holds the target (All-Reduce SUM);
+    (4) loss = log S + m - z_y. Returns (loss, m, S) per token."""
+    X = np.asarray(X, np.float64)
+    zs = [X @ np.asarray(W, np.float64) for W in W_shards]
+    m = np.max([z.max(axis=1) for z in zs], axis=0)                       # step 1
+    S = np.sum([np.exp(z - m[:, None]).sum(axis=1) for z in zs], axis=0)  # step 2
+    y = np.asarray(targets, np.int64)
+    zy = np.zeros(X.shape[0])
+    start = 0
+    for z in zs:                                                          # step 3
+        local = y - start
+        inside = (local >= 0) & (local < z.shape[1])
+        zy += np.where(inside, z[np.arange(z.shape[0]), np.clip(local, 0, z.shape[1] - 1)], 0.0)
+        start += z.shape[1]
+    return np.log(S) + m - zy, m, S                                       # step 4
+
+
+def vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss):
+    """Rank i's backward, local given the global m and S: dl/dz_v =
+    softmax(z)_v - 1[v = y] on its vocab range, scaled by the upstream dloss
+    per token; then the column-parallel backward dX_part = dZ W_i^T ({U}),
+    dW_i = X^T dZ. Returns (dZ, dX_part, dW_i)."""
+    X = np.asarray(X, np.float64)
+    W_i = np.asarray(W_i, np.float64)
+    z = X @ W_i
+    p = np.exp(z - np.asarray(m, np.float64)[:, None]) / np.asarray(S, np.float64)[:, None]
+    y = np.asarray(targets, np.int64) - vocab_start
+    rows = np.nonzero((y >= 0) & (y < z.shape[1]))[0]
+    p[rows, y[rows]] -= 1.0
+    dZ = p * np.asarray(dloss, np.float64)[:, None]
+    return dZ, dZ @ W_i.T, X.T @ dZ
 
 
 # ---------------------------------------------------------------------------
