@@ -426,6 +426,36 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
                                    "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
     del Wrs, WOs, X, O, dQKV, dY, W_r, W_O
 
+    # --- Llama-3-70B vocab-parallel LM head + fused cross-entropy, one shard of 8 ---
+    lw = synth.WORKLOADS["llama70b_lm_head_t8"]
+    v_loc = lw.extra["V_pad"] // lw.t
+    dl = synth.vocab_ce_inputs(lw.seed, lw.N, lw.h, v_loc, lw.extra["V"])
+    Xl, Wl = to_dev(dl["X"]), to_dev(dl["W_i"])
+    yl = torch.from_numpy(dl["targets"]).to(dev)
+    dlo = torch.from_numpy(dl["dloss"]).to(dev)
+    fl_ce = 2 * lw.N * lw.h * v_loc
+    stats = {}
+
+    def ce_fwd():
+        stats["s"] = T.tp_vocab_ce_fwd(Xl, Wl, yl, 0)
+
+    ms_f = time_fn(ce_fwd, reps)[0]
+    loss, m_ce, S_ce = T.tp_vocab_ce_combine(*(st[None] for st in stats["s"]))
+    dZl = torch.empty((lw.N, v_loc), dtype=bf, device=dev)
+    dXl = torch.empty((lw.N, lw.h), dtype=f32, device=dev)
+    dWl = torch.empty((lw.h, v_loc), dtype=f32, device=dev)
+
+    def ce_bwd():
+        T.tp_vocab_ce_bwd(Xl, Wl, yl, 0, m_ce, S_ce, dlo, dZ=dZl, dX_part=dXl, dW_i=dWl)
+
+    ms_b = time_fn(ce_bwd, reps)[0]
+    res["lm_head_ce_fwd"] = {"ms": round(ms_f, 4), "gflop": round(fl_ce / 1e9, 2),
+                             "tflops": round(fl_ce / (ms_f * 1e-3) / 1e12, 1),
+                             "logit_bytes_not_written": 4 * lw.N * v_loc}
+    res["lm_head_ce_bwd"] = {"ms": round(ms_b, 4), "gflop": round(3 * fl_ce / 1e9, 2),
+                             "tflops": round(3 * fl_ce / (ms_b * 1e-3) / 1e12, 1)}
+    del Xl, Wl, dZl, dXl, dWl, stats
+
     # --- GPT-style GeLU MLP shard, t = 4, forward ---
     g = synth.WORKLOADS["gpt_gelu_t4"]
     dg = synth.mlp_inputs(g.seed, g.N, g.h, g.F, g.t, "gelu")

@@ -217,6 +217,52 @@ tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h,
                                 int32_t t, void* stream);
 
 /*
+ * Vocab-parallel LM head with fused cross-entropy, one rank's share
+ * ([TPSP] "词表并行：embedding 与交叉熵", "LM head 与交叉熵"): W_out [h, V] is
+ * split by columns; rank i holds vocab ids [vocab_start, vocab_start + v_loc)
+ * (v_loc = V/t, the vocabulary padded so that it divides into multiples of
+ * 64). Its logits z = X W_i [N, v_loc] are never written to memory.
+ *   X bf16 [N,h], W_i bf16 [h,v_loc], targets int32 [N] (vocab ids over the
+ *   whole vocabulary; 4-byte aligned).
+ *   m_i, s_i, zy_i f32 [N]: per token the local max of z, sum of
+ *   exp(z - m_i) over the rank's range, and z of the target when the target
+ *   is in the range (0 otherwise).
+ * Uses the library's per-stream workspace for per-tile records
+ * (N * 2 * ceil(v_loc / 224) * 12 bytes).
+ */
+tp_status tp_vocab_ce_fwd(const void* X, const void* W_i, const int32_t* targets,
+                          int64_t vocab_start, int64_t N, int64_t h, int64_t v_loc,
+                          float* m_i, float* s_i, float* zy_i, void* stream);
+
+/*
+ * The exchange of the fused cross-entropy, on one device (the page's three
+ * All-Reduces of [N]-sized statistics: MAX of the local maxima, SUM of the
+ * exponential sums, SUM of the target logits): the t ranks' statistics,
+ * stacked f32 [t][N] in rank order, give per token m = max_i m_i,
+ * S = sum_i s_i exp(m_i - m) (each rank's sum rescaled to the global max),
+ * z_y = sum_i zy_i, and loss = log S + m - z_y.
+ *   loss f32 [N]; m, S f32 [N] (either may be NULL) for the backward.
+ */
+tp_status tp_vocab_ce_combine(const float* m_parts, const float* s_parts,
+                              const float* zy_parts, int32_t t, int64_t N,
+                              float* loss, float* m, float* S, void* stream);
+
+/*
+ * Backward of one rank's share, local given the global m and S ([TPSP] "LM
+ * head 与交叉熵": dl/dz_v = softmax(z)_v - 1[v = y]):
+ *   dZ bf16 [N,v_loc] = (exp(z - m) / S - one-hot(target)) * dloss, with z
+ *   recomputed as X W_i (dZ is caller-owned scratch, like dH);
+ *   dX_part f32 [N,h] = dZ W_i^T ({U}; accumulate = 1 adds into it);
+ *   dW_i f32 [h,v_loc] = X^T dZ.
+ *   m, S, dloss f32 [N] (dloss: the upstream gradient of each token's loss).
+ */
+tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets,
+                          int64_t vocab_start, const float* m, const float* S,
+                          const float* dloss, int64_t N, int64_t h, int64_t v_loc,
+                          void* dZ, float* dX_part, float* dW_i, int accumulate,
+                          void* stream);
+
+/*
  * Shard arithmetic of a tensor over a device mesh ([SB6] §6.1): host only,
  * no device work. A[I_{XY}, J] splits dim I over mesh axes X and Y (divided
  * by their product); axes no dim uses replicate the shard.

@@ -70,7 +70,7 @@ def digest(a: np.ndarray) -> str:
 class Workload:
     """A named workload: shapes, TP degree and seed (no arithmetic)."""
     name: str
-    kind: str           # "mlp" | "qkv" | "mlp_bwd"
+    kind: str           # "mlp" | "qkv" | "mlp_bwd" | "vocab_ce"
     seed: int
     N: int              # tokens (b*s)
     h: int
@@ -101,6 +101,10 @@ WORKLOADS = {
     # backward of the Llama-3-70B SwiGLU MLP shard
     "llama70b_swiglu_t8_bwd": Workload("llama70b_swiglu_t8_bwd", "mlp_bwd", 4, N=4096, h=8192,
                                        F=28672, t=8, act="swiglu"),
+    # Llama-3-70B vocab-parallel LM head, one shard of eight: V = 128256 padded
+    # to a multiple of 128 t = 1024 (129024), 16128 vocab ids per rank
+    "llama70b_lm_head_t8": Workload("llama70b_lm_head_t8", "vocab_ce", 5, N=4096, h=8192, t=8,
+                                    extra={"V": 128256, "V_pad": 129024}),
 }
 
 
@@ -154,6 +158,19 @@ def qkv_inputs(seed: int, N: int, h: int, n_h: int, n_kv: int, d_h: int, t: int)
     dQKV = draw(rng, (N, width // t))
     dY = draw(rng, (N, h))
     return {"X": X, "W_qkv": W_qkv, "W_O": W_O, "O": O, "dQKV": dQKV, "dY": dY}
+
+
+def vocab_ce_inputs(seed: int, N: int, h: int, v_loc: int, V: int):
+    """One rank's LM-head inputs: X[N,h] ~ N(0,1), its weight shard
+    W_i[h,v_loc] (fan_in h), the token targets (uniform over the V real vocab
+    ids, int32; padded ids never occur) and the upstream gradient of each
+    token's loss (1/N: the mean loss)."""
+    rng = np.random.default_rng(seed)
+    X = draw(rng, (N, h))
+    W_i = draw(rng, (h, v_loc), fan_in=h)
+    targets = rng.integers(0, V, size=N).astype(np.int32)
+    dloss = np.full(N, 1.0 / N, dtype=np.float32)
+    return {"X": X, "W_i": W_i, "targets": targets, "dloss": dloss}
 
 
 def int_inputs(seed: int, shape, lo: int = -2, hi: int = 2) -> np.ndarray:

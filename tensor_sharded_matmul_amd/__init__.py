@@ -63,6 +63,10 @@ def load():
         "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
         "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
         "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], ctypes.c_int),
+        "tp_vocab_ce_fwd": ([vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp], ctypes.c_int),
+        "tp_vocab_ce_combine": ([vp, vp, vp, i32, i64, vp, vp, vp, vp], ctypes.c_int),
+        "tp_vocab_ce_bwd": ([vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp, vp, ctypes.c_int, vp],
+                            ctypes.c_int),
         "tp_shard_shape": ([i32, ctypes.POINTER(i64), i32, i32, ctypes.POINTER(i64),
                             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64),
                             ctypes.POINTER(i64), ctypes.POINTER(i64)], ctypes.c_int),
@@ -277,6 +281,52 @@ def tp_kv_grad_accumulate(dW_dst, dW_src, n_h, n_kv, d_h, t, stream=None):
     _dev(dW_src, "dW_src", _f32, (h, w))
     _check(lib.tp_kv_grad_accumulate(_ptr(dW_dst), _ptr(dW_src), h, n_h, n_kv, d_h, t, _stream(stream)))
     return dW_dst
+
+
+def tp_vocab_ce_fwd(X, W_i, targets, vocab_start, stream=None):
+    """One rank's local cross-entropy statistics; returns (m_i, s_i, zy_i), f32 [N]."""
+    lib = load()
+    N, h = X.shape
+    v_loc = W_i.shape[1]
+    _dev(X, "X", _bf16, (N, h))
+    _dev(W_i, "W_i", _bf16, (h, v_loc))
+    _dev(targets, "targets", torch.int32, (N,))
+    m, s, zy = (torch.empty((N,), dtype=_f32, device=X.device) for _ in range(3))
+    _check(lib.tp_vocab_ce_fwd(_ptr(X), _ptr(W_i), _ptr(targets), vocab_start, N, h, v_loc, _ptr(m), _ptr(s),
+                               _ptr(zy), _stream(stream)))
+    return m, s, zy
+
+
+def tp_vocab_ce_combine(m_parts, s_parts, zy_parts, stream=None):
+    """Stacked [t, N] local statistics -> (loss, m, S), f32 [N]."""
+    lib = load()
+    t, N = m_parts.shape
+    for name, x in (("m_parts", m_parts), ("s_parts", s_parts), ("zy_parts", zy_parts)):
+        _dev(x, name, _f32, (t, N))
+    loss, m, S = (torch.empty((N,), dtype=_f32, device=m_parts.device) for _ in range(3))
+    _check(lib.tp_vocab_ce_combine(_ptr(m_parts), _ptr(s_parts), _ptr(zy_parts), t, N, _ptr(loss), _ptr(m),
+                                   _ptr(S), _stream(stream)))
+    return loss, m, S
+
+
+def tp_vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss, dZ=None, dX_part=None, dW_i=None,
+                    accumulate=False, stream=None):
+    """One rank's backward; returns (dZ, dX_part, dW_i)."""
+    lib = load()
+    N, h = X.shape
+    v_loc = W_i.shape[1]
+    _dev(X, "X", _bf16, (N, h))
+    _dev(W_i, "W_i", _bf16, (h, v_loc))
+    _dev(targets, "targets", torch.int32, (N,))
+    for name, x in (("m", m), ("S", S), ("dloss", dloss)):
+        _dev(x, name, _f32, (N,))
+    dZ = _out(dZ, "dZ", _bf16, (N, v_loc), X)
+    dX_part = _out(dX_part, "dX_part", _f32, (N, h), X)
+    dW_i = _out(dW_i, "dW_i", _f32, (h, v_loc), X)
+    _check(lib.tp_vocab_ce_bwd(_ptr(X), _ptr(W_i), _ptr(targets), vocab_start, _ptr(m), _ptr(S), _ptr(dloss), N,
+                               h, v_loc, _ptr(dZ), _ptr(dX_part), _ptr(dW_i), int(bool(accumulate)),
+                               _stream(stream)))
+    return dZ, dX_part, dW_i
 
 
 def tp_shard_shape(shape, elem_bytes, axis_sizes, dim_axis_mask):

@@ -82,6 +82,8 @@ enum Epi : int {
     EPI_SWIGLU = 3,     // C bf16 = SiLU(g)*u; C2 bf16 = [g | u] (optional)
     EPI_GELU_BWD = 4,   // C bf16 = acc * GeLU'(aux)
     EPI_SWIGLU_BWD = 5, // C bf16 = [acc*u*SiLU'(g) | acc*SiLU(g)], aux = [g|u]
+    EPI_CE_STATS = 6,   // logits -> per (row, wave column block) {max, sum exp(z - max), z_target}
+    EPI_CE_GRAD = 7,    // C bf16 = (exp(acc - m) / S - [col = target]) * dloss, per row
 };
 
 struct GemmArgs {
@@ -100,7 +102,18 @@ struct GemmArgs {
     // of K (a multiple of 64; the last split ends at K); split s writes its
     // fp32 partial to C + s * M * ldc. ksplit = 1: the whole K, C as given.
     int ksplit, kper;
+    // Cross-entropy epilogues: per-row target vocab id (tgt), the vocab id of
+    // column 0 (col0); EPI_CE_GRAD also the per-row max m (rm), sum S (rs)
+    // and upstream gradient (rd). EPI_CE_STATS writes 3-float records to C,
+    // ldc records per row.
+    const int* tgt;
+    const float *rm, *rs, *rd;
+    int col0;
 };
+
+// Output columns per tile of the cross-entropy statistics GEMM (2 waves of
+// 112 columns each write one record per row).
+constexpr int kCeTileN = 224;
 
 // Token rows of the tile a split-K product of M rows runs with.
 inline int splitk_tile_m(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
@@ -387,10 +400,109 @@ __device__ __forceinline__ void epilogue_act_bwd(const f32x4_t (&acc)[MI][NI], c
     });
 }
 
+// Vocab-parallel cross-entropy, forward: the logits never leave registers.
+// For each row, the 4 lanes that hold it (lane, lane ^ 16, lane ^ 32,
+// lane ^ 48) reduce this wave's 16 NI columns to the record
+// {max z, sum exp(z - max), z of the target column (0 if not here)}, written
+// to record `part` of the row, part = the wave's column block index across
+// the grid (tile column x waves per tile row + wave column). One pass over
+// the accumulators: a running maximum with the running sum rescaled when it
+// grows (4 logits live at a time, so the 256 accumulators need no copies).
+__device__ __forceinline__ void ce_merge(float& m, float& s, float m2, float s2) {
+    const float mx = fmaxf(m, m2);
+    if (mx == -__builtin_inff()) return;  // both empty
+    s = s * __expf(m - mx) + s2 * __expf(m2 - mx);
+    m = mx;
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_ce_stats(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,
+                                                  int nb) {
+    const int lane = threadIdx.x & 63;
+    const int part = (nb - 4 * (lane >> 4)) / (16 * NI);
+    float* rec = static_cast<float*>(args.C);
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int m = mb + i * 16;
+        const int yt = args.tgt[m < args.M ? m : 0] - args.col0 - nb;  // target column - this lane's first
+        float run_m = -__builtin_inff(), run_s = 0.f, zy = 0.f;
+        static_for<0, NI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const f32x4_t v = acc[i][j];
+            float gm = -__builtin_inff();
+            static_for<0, 4>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                if (nb + 16 * j + r < args.N) {
+                    gm = fmaxf(gm, v[r]);
+                    if (yt == 16 * j + r) zy = v[r];
+                }
+            });
+            if (gm != -__builtin_inff()) {
+                const float mx = fmaxf(run_m, gm);
+                float gs = 0.f;
+                static_for<0, 4>([&](auto rc) {
+                    constexpr int r = decltype(rc)::value;
+                    if (nb + 16 * j + r < args.N) gs += __expf(v[r] - mx);
+                });
+                run_s = run_s * __expf(run_m - mx) + gs;
+                run_m = mx;
+            }
+        });
+        ce_merge(run_m, run_s, __shfl_xor(run_m, 16, 64), __shfl_xor(run_s, 16, 64));
+        ce_merge(run_m, run_s, __shfl_xor(run_m, 32, 64), __shfl_xor(run_s, 32, 64));
+        zy += __shfl_xor(zy, 16, 64);
+        zy += __shfl_xor(zy, 32, 64);
+        if ((lane >> 4) == 0 && m < args.M) {
+            float* p = rec + ((size_t)m * args.ldc + part) * 3;
+            p[0] = run_m;
+            p[1] = run_s;
+            p[2] = zy;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Vocab-parallel cross-entropy, backward: dZ = (softmax(z) - one-hot) * dloss
+// with the global per-row max and sum (bf16 store).
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_ce_grad(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,
+                                                 int nb) {
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int m = mb + i * 16;
+        if (m < args.M) {
+            const float mm = args.rm[m], inv = 1.0f / args.rs[m], dl = args.rd[m];
+            const int yt = args.tgt[m] - args.col0;
+            uint16_t* crow = static_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
+            static_for<0, NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int n = nb + 16 * j;
+                if (n < args.N) {
+                    float g[4];
+                    static_for<0, 4>([&](auto rc) {
+                        constexpr int r = decltype(rc)::value;
+                        g[r] = (__expf(acc[i][j][r] - mm) * inv - (n + r == yt ? 1.0f : 0.0f)) * dl;
+                    });
+                    *reinterpret_cast<u32x2_t*>(crow + n) = pack4(g[0], g[1], g[2], g[3]);
+                }
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 template <int MI, int NI, int EPI>
 __device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb, int nb) {
     if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD) {
         epilogue_act_bwd<MI, NI, EPI>(acc, args, mb, nb);
+        return;
+    }
+    if constexpr (EPI == EPI_CE_STATS) {
+        epilogue_ce_stats<MI, NI>(acc, args, mb, nb);
+        return;
+    }
+    if constexpr (EPI == EPI_CE_GRAD) {
+        epilogue_ce_grad<MI, NI>(acc, args, mb, nb);
         return;
     }
     static_for<0, MI>([&](auto ic) {

@@ -88,15 +88,9 @@ inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int kspli
     return best;
 }
 
+// Every other product: the tile shape and ring for its layout and size.
 template <bool A_T, bool B_KN, int EPI>
-tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
-    if (a.M == 0 || a.N == 0) return TP_OK;
-    const int64_t a_bytes = (int64_t)(A_T ? a.K : a.M) * a.lda * 2;
-    const int64_t b_bytes = (int64_t)(B_KN ? a.K : a.N) * a.ldb * 2;
-    if (a_bytes > kMaxOperandBytes || b_bytes > kMaxOperandBytes)
-        return fail(TP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
-    a.a_bytes = (uint32_t)a_bytes;
-    a.b_bytes = (uint32_t)b_bytes;
+tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
     constexpr bool SW = (EPI == EPI_SWIGLU);
     using Sq = CfgOf<A_T, B_KN, 256, 256, 256, 256, 2, 2>;
     using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
@@ -125,6 +119,28 @@ tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
             else return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
         default:
             return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
+    }
+}
+
+
+template <bool A_T, bool B_KN, int EPI>
+tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
+    if (a.M == 0 || a.N == 0) return TP_OK;
+    const int64_t a_bytes = (int64_t)(A_T ? a.K : a.M) * a.lda * 2;
+    const int64_t b_bytes = (int64_t)(B_KN ? a.K : a.N) * a.ldb * 2;
+    if (a_bytes > kMaxOperandBytes || b_bytes > kMaxOperandBytes)
+        return fail(TP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+    a.a_bytes = (uint32_t)a_bytes;
+    a.b_bytes = (uint32_t)b_bytes;
+    if constexpr (EPI == EPI_CE_STATS) {
+        using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
+        // one record per row for each 112-column wave block of 256 x 224
+        // tiles (kCeTileN; the 256 x 256 tile would spill a register): the
+        // host sizes its record buffer for exactly this shape
+        static_assert(N224::TN == kCeTileN, "record layout");
+        return launch_cfg<N224, A_T, B_KN, EPI>(fn, a, s);
+    } else {
+        return launch_by_shape<A_T, B_KN, EPI>(fn, a, s);
     }
 }
 

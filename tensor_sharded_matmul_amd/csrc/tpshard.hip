@@ -392,6 +392,58 @@ __global__ void __launch_bounds__(256) kv_grad_accumulate_kernel(float* __restri
     }
 }
 
+// Vocab-parallel cross-entropy: the rank's local statistics from the GEMM's
+// per-(row, wave column block) records {max, sum exp(z - max), z_target}.
+// One wave per row: m = max over records, s = sum_p s_p exp(m_p - m),
+// z_y = sum_p z_p (one record at most holds the target).
+__global__ void __launch_bounds__(256) ce_stats_merge_kernel(const float* __restrict__ rec, int nparts, int M,
+                                                             float* __restrict__ m_out, float* __restrict__ s_out,
+                                                             float* __restrict__ zy_out) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // whole waves leave together
+    const float* r = rec + (size_t)row * nparts * 3;
+    float m = -__builtin_inff();
+    for (int p = lane; p < nparts; p += 64) m = fmaxf(m, r[3 * p]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float s = 0.f, zy = 0.f;
+    for (int p = lane; p < nparts; p += 64) {
+        const float mp = r[3 * p];
+        if (mp != -__builtin_inff()) s += r[3 * p + 1] * __expf(mp - m);
+        zy += r[3 * p + 2];
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        s += __shfl_xor(s, off, 64);
+        zy += __shfl_xor(zy, off, 64);
+    }
+    if (lane == 0) {
+        m_out[row] = m;
+        s_out[row] = s;
+        zy_out[row] = zy;
+    }
+}
+
+// The exchange of the fused cross-entropy on one device: for each token the
+// t ranks' local statistics (stacked [t][N]) give m = max_i m_i,
+// S = sum_i s_i exp(m_i - m), z_y = sum_i z_y,i and loss = log S + m - z_y.
+__global__ void __launch_bounds__(256) ce_combine_kernel(const float* __restrict__ mp, const float* __restrict__ sp,
+                                                         const float* __restrict__ zp, int t, int64_t N,
+                                                         float* __restrict__ loss, float* __restrict__ m_out,
+                                                         float* __restrict__ S_out) {
+    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += (int64_t)gridDim.x * blockDim.x) {
+        float m = -__builtin_inff();
+        for (int i = 0; i < t; ++i) m = fmaxf(m, mp[i * N + n]);
+        float S = 0.f, zy = 0.f;
+        for (int i = 0; i < t; ++i) {
+            S += sp[i * N + n] * __expf(mp[i * N + n] - m);
+            zy += zp[i * N + n];
+        }
+        loss[n] = __logf(S) + m - zy;
+        if (m_out) m_out[n] = m;
+        if (S_out) S_out[n] = S;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Fused-QKV regroup: a bit-exact gather of three contiguous column runs per
 // row. A workgroup moves kRegroupRows whole output rows as 16-byte chunks in
@@ -705,6 +757,98 @@ tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h, i
                        dW_dst, dW_src, h, (int)ld, c0, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// Common checks of the vocab-parallel cross-entropy calls.
+static tp_status check_ce(const char* fn, int64_t N, int64_t h, int64_t v_loc, int64_t vocab_start,
+                          const int32_t* targets) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "v_loc", v_loc));
+    if (vocab_start < 0 || vocab_start + v_loc > 0x7fffffffLL)
+        return fail(TP_ERR_INVALID_ARG, "%s: vocab range [%lld, %lld) outside int32", fn, (long long)vocab_start,
+                    (long long)(vocab_start + v_loc));
+    if (N > 0 && (targets == nullptr || (reinterpret_cast<uintptr_t>(targets) & 3u)))
+        return fail(TP_ERR_INVALID_ARG, "%s: targets is NULL or not 4-byte aligned", fn);
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, v_loc));
+    TP_TRY(check_elems(fn, N, v_loc));
+    return TP_OK;
+}
+
+tp_status tp_vocab_ce_fwd(const void* X, const void* W_i, const int32_t* targets, int64_t vocab_start, int64_t N,
+                          int64_t h, int64_t v_loc, float* m_i, float* s_i, float* zy_i, void* stream) {
+    const char* fn = "tp_vocab_ce_fwd";
+    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start, targets));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W_i, "W_i");
+    TP_CHECK_TOK_PTR(m_i, "m_i");
+    TP_CHECK_TOK_PTR(s_i, "s_i");
+    TP_CHECK_TOK_PTR(zy_i, "zy_i");
+    if (N == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // records: 2 wave column blocks per kCeTileN-wide tile (launch_gemm runs
+    // EPI_CE_STATS with 256 x 224 tiles of 2 x 2 waves)
+    const int nparts = (int)(2 * ((v_loc + kCeTileN - 1) / kCeTileN));
+    float* rec = nullptr;
+    TP_TRY(workspace(fn, s, (size_t)N * nparts * 3 * sizeof(float), &rec));
+    GemmArgs a = make_args(X, W_i, rec, (int)N, (int)v_loc, (int)h, (int)h, (int)v_loc, nparts);
+    a.tgt = targets;
+    a.col0 = (int)vocab_start;
+    TP_TRY((launch_gemm<false, true, EPI_CE_STATS>(fn, a, s)));
+    hipLaunchKernelGGL(ce_stats_merge_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, rec, nparts, (int)N,
+                       m_i, s_i, zy_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+tp_status tp_vocab_ce_combine(const float* m_parts, const float* s_parts, const float* zy_parts, int32_t t,
+                              int64_t N, float* loss, float* m, float* S, void* stream) {
+    const char* fn = "tp_vocab_ce_combine";
+    if (t <= 0) return fail(TP_ERR_INVALID_ARG, "%s: t = %d must be positive", fn, t);
+    TP_TRY(check_tokens(fn, N));
+    if (N == 0) return ok();
+    if (!m_parts || !s_parts || !zy_parts || !loss)
+        return fail(TP_ERR_INVALID_ARG, "%s: m_parts, s_parts, zy_parts and loss must not be NULL", fn);
+    TP_TRY(check_elems(fn, t, N));
+    const unsigned blocks = (unsigned)std::min<int64_t>((N + 255) / 256, 8192);
+    hipLaunchKernelGGL(ce_combine_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), m_parts,
+                       s_parts, zy_parts, (int)t, N, loss, m, S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets, int64_t vocab_start,
+                          const float* m, const float* S, const float* dloss, int64_t N, int64_t h, int64_t v_loc,
+                          void* dZ, float* dX_part, float* dW_i, int accumulate, void* stream) {
+    const char* fn = "tp_vocab_ce_bwd";
+    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start, targets));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W_i, "W_i");
+    TP_CHECK_TOK_PTR(dZ, "dZ");
+    TP_CHECK_TOK_PTR(dX_part, "dX_part");
+    TP_CHECK_PTR(dW_i, "dW_i");
+    if (N > 0 && (!m || !S || !dloss))
+        return fail(TP_ERR_INVALID_ARG, "%s: m, S and dloss must not be NULL", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // dZ = (softmax(X W_i) - one-hot) * dloss, the logits recomputed
+    GemmArgs a = make_args(X, W_i, dZ, (int)N, (int)v_loc, (int)h, (int)h, (int)v_loc, (int)v_loc);
+    a.tgt = targets;
+    a.col0 = (int)vocab_start;
+    a.rm = m;
+    a.rs = S;
+    a.rd = dloss;
+    // dX_part = dZ W_i^T (NT, {U}); dW_i = X^T dZ (TN)
+    GemmArgs b = make_args(dZ, W_i, dX_part, (int)N, (int)h, (int)v_loc, (int)v_loc, (int)v_loc, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    GemmArgs c = make_args(X, dZ, dW_i, (int)h, (int)v_loc, (int)N, (int)h, (int)v_loc, (int)v_loc);
+    TP_TRY(reserve(fn, s, {plan_of<false, false, EPI_F32>(b), plan_of<true, true, EPI_F32>(c)}));
+    TP_TRY((launch_gemm<false, true, EPI_CE_GRAD>(fn, a, s)));
+    TP_TRY((run_gemm<false, false, EPI_F32>(fn, b, s)));
+    TP_TRY((run_gemm<true, true, EPI_F32>(fn, c, s)));
     return ok();
 }
 
