@@ -284,6 +284,20 @@ def main() -> int:
                 "flop_per_launch": fl[dom], "avg_launch_ms": round(per_launch_ms, 4)}
     log(f"[bench] dominant {dom}: {per_launch_ms:.4f} ms per launch, {achieved:.1f} TFLOP/s")
 
+    # GEMM2 computed in token-row chunks with an event per chunk (the schedule
+    # that lets the exchange of chunk c overlap chunk c + 1): its overhead
+    chunked = {}
+    for nc in (2, 4, 8):
+        evs = [torch.cuda.Event() for _ in range(nc)]
+
+        def g2c():
+            T.tp_row_linear_partial_chunked(Z, W_out, nc, P=P, events=evs)
+
+        ms_c = time_fn(g2c, args.reps)[0]
+        chunked[str(nc)] = {"ms": round(ms_c, 4), "tflops": round(fl["gemm2_down_partial"] / (ms_c * 1e-3) / 1e12, 1),
+                            "overhead": round(ms_c / kt["gemm2_down_partial"]["ms"] - 1, 3)}
+    kt["gemm2_down_partial_chunked"] = chunked
+
     rows = {"mlp_kernels": kt,
             "fwd_ms": round(time_fn(fwd, args.reps)[0], 4), "bwd_ms": round(bwd_mean, 4)}
     rows["fwd_tflops"] = round(fwd_flops / (rows["fwd_ms"] * 1e-3) / 1e12, 1)

@@ -114,6 +114,21 @@ tp_status tp_row_linear_partial(const void* Z, const void* W, float* P,
                                 int accumulate, void* stream);
 
 /*
+ * The row-parallel partial computed in row chunks, for overlapping its
+ * exchange with the product ([SB6] §6.6 / [TPSP] "把通信藏到计算后面": the
+ * reduction of chunk c can run while chunk c + 1 is computed). The result is
+ * that of tp_row_linear_partial. Token rows are cut into nchunks chunks of
+ * ceil(N / nchunks) rows rounded up to 16 (the last may be shorter or
+ * empty); after chunk c is enqueued, events[c] (a caller-created hipEvent_t)
+ * is recorded on `stream`, so another stream can wait for exactly that
+ * chunk. events may be NULL (no events). 1 <= nchunks <= 64.
+ */
+tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P,
+                                        int64_t N, int64_t k_loc, int64_t n,
+                                        int accumulate, int32_t nchunks,
+                                        void* const* events, void* stream);
+
+/*
  * One rank's MLP share, forward ([TPSP] "MLP：先列后行，只通信一次"): first
  * matrix column-split with the activation applied locally, second matrix
  * row-split, giving the partial sum of the layer output.

@@ -63,6 +63,8 @@ def load():
         "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
         "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
         "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], ctypes.c_int),
+        "tp_row_linear_partial_chunked": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, i32,
+                                           ctypes.POINTER(vp), vp], ctypes.c_int),
         "tp_vocab_ce_fwd": ([vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp], ctypes.c_int),
         "tp_vocab_ce_combine": ([vp, vp, vp, i32, i64, vp, vp, vp, vp], ctypes.c_int),
         "tp_vocab_ce_bwd": ([vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp, vp, ctypes.c_int, vp],
@@ -161,6 +163,28 @@ def tp_row_linear_partial(Z, W, P=None, accumulate=False, stream=None):
     P = _out(P, "P", _f32, (N, n), Z)
     _check(lib.tp_row_linear_partial(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
                                      _stream(stream)))
+    return P
+
+
+def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, events=None, stream=None):
+    """P = Z W (or P += Z W) in nchunks token-row chunks; events: None or nchunks
+    torch.cuda.Event objects, each recorded after its chunk. Returns P."""
+    lib = load()
+    N, k_loc = Z.shape
+    n = W.shape[1]
+    _dev(Z, "Z", _bf16, (N, k_loc))
+    _dev(W, "W", _bf16, (k_loc, n))
+    P = _out(P, "P", _f32, (N, n), Z)
+    ev = None
+    if events is not None:
+        if len(events) != nchunks:
+            raise ValueError(f"{len(events)} events for {nchunks} chunks")
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event on its first record
+                e.record()
+        ev = (ctypes.c_void_p * nchunks)(*[e.cuda_event for e in events])
+    _check(lib.tp_row_linear_partial_chunked(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
+                                             nchunks, ev, _stream(stream)))
     return P
 
 

@@ -548,6 +548,49 @@ tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t 
     return st == TP_OK ? ok() : st;
 }
 
+tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc,
+                                        int64_t n, int accumulate, int32_t nchunks, void* const* events,
+                                        void* stream) {
+    const char* fn = "tp_row_linear_partial_chunked";
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k_loc", k_loc));
+    TP_TRY(check_width(fn, "n", n));
+    if (nchunks < 1 || nchunks > 64) return fail(TP_ERR_INVALID_ARG, "%s: nchunks = %d outside [1, 64]", fn, nchunks);
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(P, "P");
+    TP_TRY(check_elems(fn, N, k_loc));
+    TP_TRY(check_elems(fn, k_loc, n));
+    TP_TRY(check_elems(fn, N, n));
+    if (events)
+        for (int c = 0; c < nchunks; ++c)
+            if (!events[c]) return fail(TP_ERR_INVALID_ARG, "%s: events[%d] is NULL", fn, c);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // chunk c: token rows [c rows, (c + 1) rows), rows a multiple of 16
+    const int64_t rows = ((N + nchunks - 1) / nchunks + 15) / 16 * 16;
+    auto chunk = [&](int c) {
+        const int64_t r0 = std::min<int64_t>(N, c * rows), r1 = std::min<int64_t>(N, r0 + rows);
+        GemmArgs a = make_args(static_cast<const uint16_t*>(Z) + r0 * k_loc, W, P + r0 * n, (int)(r1 - r0), (int)n,
+                               (int)k_loc, (int)k_loc, (int)n, (int)n);
+        a.accumulate = accumulate ? 1 : 0;
+        return a;
+    };
+    size_t ws = 0;
+    for (int c = 0; c < nchunks; ++c) ws = std::max(ws, plan_of<false, true, EPI_F32>(chunk(c)).bytes);
+    if (ws) {
+        float* p = nullptr;
+        TP_TRY(workspace(fn, s, ws, &p));
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        TP_TRY((run_gemm<false, true, EPI_F32>(fn, chunk(c), s)));
+        if (events) {
+            hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[c]), s);
+            if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: event %d: %s", fn, c, hipGetErrorString(e));
+        }
+    }
+    return ok();
+}
+
 tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, int64_t N, int64_t h,
                            int64_t f, int act, void* Z, void* H_save, float* P, int accumulate,
                            void* stream) {

@@ -1,0 +1,44 @@
+"""The row-parallel partial in row chunks (tp_row_linear_partial_chunked):
+exact against the oracle on integer inputs for several chunk counts (chunks
+that need split-K included), with and without accumulate, every chunk's event
+recorded in chunk order; at the Llama-3-70B GEMM2 shape, equal to the
+unchunked call within the tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import tensor_sharded_matmul_amd as T
+from gpu_util import TOL, err, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,k,n,nchunks", [(1000, 512, 640, 1), (1000, 512, 640, 3), (1000, 2048, 640, 8),
+                                           (37, 256, 128, 4), (300, 4096, 320, 2)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_chunked_partial_exact(N, k, n, nchunks, accumulate):
+    Zb, Wb = synth.int_inputs(80, (N, k)), synth.int_inputs(81, (k, n))
+    P0 = synth.bf16_to_f64(synth.int_inputs(82, (N, n)))
+    P = torch.from_numpy(P0.astype(np.float32)).to("cuda:0")
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nchunks)]
+    T.tp_row_linear_partial_chunked(to_dev(Zb), to_dev(Wb), nchunks, P=P, accumulate=accumulate, events=events)
+    torch.cuda.synchronize()
+    want = O.row_linear_partial(synth.bf16_to_f64(Zb), synth.bf16_to_f64(Wb)) + (P0 if accumulate else 0)
+    assert np.array_equal(f64(P), want)
+    assert all(e.query() for e in events)
+    for a, b in zip(events, events[1:]):
+        assert a.elapsed_time(b) >= 0.0
+
+
+def test_chunked_matches_unchunked_llama_gemm2():
+    w = synth.WORKLOADS["llama70b_swiglu_t8"]
+    rng = np.random.default_rng(9)
+    Z = to_dev(synth.draw(rng, (w.N, w.f)))
+    W = to_dev(synth.draw(rng, (w.f, w.h), fan_in=w.F))
+    ref = T.tp_row_linear_partial(Z, W)
+    for nchunks in (2, 4, 8):
+        got = T.tp_row_linear_partial_chunked(Z, W, nchunks)
+        torch.cuda.synchronize()
+        assert err(f64(got), f64(ref)) <= TOL, nchunks
