@@ -18,7 +18,7 @@ __all__ = [
     "mlp_shard_bwd_cols", "col_linear_bwd", "row_linear_bwd",
     "qkv_regroup_index", "qkv_regroup", "naive_split_index", "shard_shape",
     "kv_heads_of_rank", "kv_replica_ranks", "kv_grad_accumulate", "kv_replica_grad_sum",
-    "vocab_ce_local", "vocab_ce_loss", "vocab_ce_bwd",
+    "vocab_ce_local", "vocab_ce_loss", "vocab_ce_bwd", "vocab_embed_fwd", "vocab_embed_bwd",
     "ShardError", "llama_layer_params", "llama_model_params",
     "llama_shard_weight_shapes", "gemm_flops", "mlp_shard_flops",
     "check_heads_divisible", "rel_err",
@@ -407,6 +407,32 @@ def vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss):
     p[rows, y[rows]] -= 1.0
     dZ = p * np.asarray(dloss, np.float64)[:, None]
     return dZ, dZ @ W_i.T, X.T @ dZ
+
+
+def vocab_embed_fwd(ids, E_i, vocab_start):
+    """Rank i's masked lookup ([TPSP] "输入 embedding"): the rank holds rows
+    [vocab_start, vocab_start + V/t) of the table; a token whose id is in that
+    range gets its row, any other token a zero row. Summing the ranks' outputs
+    (the g All-Reduce) gives the full lookup. Exact copy of the bit patterns
+    (uint16 bf16 rows in, uint16 out)."""
+    E_i = np.asarray(E_i)
+    ids = np.asarray(ids, np.int64) - vocab_start
+    out = np.zeros((len(ids), E_i.shape[1]), dtype=E_i.dtype)
+    inside = (ids >= 0) & (ids < E_i.shape[0])
+    out[inside] = E_i[ids[inside]]
+    return out
+
+
+def vocab_embed_bwd(ids, dY, vocab_start, v_loc):
+    """Gradient of rank i's table rows: dE_i[v] = sum of dY[n] over the tokens
+    n whose id is vocab_start + v (rows no token uses are zero)."""
+    dY = np.asarray(dY, np.float64)
+    ids = np.asarray(ids, np.int64) - vocab_start
+    dE = np.zeros((v_loc, dY.shape[1]))
+    for n, v in enumerate(ids):
+        if 0 <= v < v_loc:
+            dE[v] += dY[n]
+    return dE
 
 
 # ---------------------------------------------------------------------------

@@ -93,3 +93,26 @@ def test_backward_matches_central_differences():
                 Wm[i][a, b] -= eps
                 fdW[a, b] = (L(X, Wp) - L(X, Wm)) / (2 * eps)
         assert np.allclose(outs[i][2], fdW, atol=1e-7)
+
+
+def test_masked_lookups_sum_to_the_one_hot_product():
+    # [TPSP] "输入 embedding": the lookup is the one-hot [N, V] times the table
+    # [V, h], split on the contraction dim V (a row-parallel layer); each
+    # token gets a non-zero row from exactly one rank
+    rng = np.random.default_rng(6)
+    N, V, h, t = 11, 20, 3, 4
+    E = rng.standard_normal((V, h))
+    ids = rng.integers(0, V, size=N)
+    ids[:2] = [0, V - 1]
+    onehot = np.zeros((N, V))
+    onehot[np.arange(N), ids] = 1.0
+    parts = [O.vocab_embed_fwd(ids, E[i * V // t:(i + 1) * V // t], i * V // t) for i in range(t)]
+    assert np.array_equal(sum(parts), onehot @ E)
+    nonzero = np.sum([np.any(p != 0, axis=1) for p in parts], axis=0)
+    assert np.all(nonzero == 1)
+    # backward: dE = onehot^T dY, per rank its own rows
+    dY = rng.standard_normal((N, h))
+    full = onehot.T @ dY
+    for i in range(t):
+        got = O.vocab_embed_bwd(ids, dY, i * V // t, V // t)
+        assert np.allclose(got, full[i * V // t:(i + 1) * V // t], atol=1e-12)
