@@ -470,6 +470,24 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
                              "tflops": round(3 * fl_ce / (ms_b * 1e-3) / 1e12, 1)}
     del Xl, Wl, dZl, dXl, dWl, stats
 
+    # --- Llama-3-70B vocab-parallel input embedding, one shard of 8 (rank 0) ---
+    gen.manual_seed(lw.seed + 1)
+    El = torch.randn((v_loc, lw.h), device=dev, generator=gen).to(bf)
+    idl = torch.from_numpy(dl["targets"]).to(dev)           # token ids, uniform over the vocabulary
+    in_range = int(((idl >= 0) & (idl < v_loc)).sum())
+    outl = torch.empty((lw.N, lw.h), dtype=bf, device=dev)
+    ms = time_graph(lambda: T.tp_vocab_embed_fwd(idl, El, 0, out=outl), 16)
+    eb = 2 * lw.h * (in_range + lw.N)   # rows read + every output row written
+    res["embed_fwd"] = {"ms": round(ms, 5), "bytes": eb, "gbs": round(eb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    dYe = torch.randn((lw.N, lw.h), device=dev, generator=gen)
+    dEl = torch.empty((v_loc, lw.h), dtype=f32, device=dev)
+    ms = time_fn(lambda: T.tp_vocab_embed_bwd(idl, dYe, 0, v_loc, dE_i=dEl), reps)[0]
+    eb = 4 * lw.h * (in_range + v_loc)  # gradient rows read + every table row written
+    res["embed_bwd"] = {"ms": round(ms, 5), "bytes": eb, "gbs": round(eb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    del El, outl, dYe, dEl
+
     # --- GPT-style GeLU MLP shard, t = 4, forward ---
     g = synth.WORKLOADS["gpt_gelu_t4"]
     dg = synth.mlp_inputs(g.seed, g.N, g.h, g.F, g.t, "gelu")

@@ -278,6 +278,32 @@ tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets
                           void* stream);
 
 /*
+ * Vocab-parallel input embedding, one rank's share ([TPSP] "输入 embedding"):
+ * the rank holds table rows [vocab_start, vocab_start + v_loc). A token whose
+ * id is in that range gets its row, any other token a zero row; the sum of
+ * the ranks' outputs (the exchange after this row-parallel layer) is the
+ * full lookup.
+ *   ids int32 [N] (4-byte aligned), E_i bf16 [v_loc, h], out bf16 [N, h].
+ *   accumulate = 0: out is overwritten (zero rows included, a bit-exact
+ *   copy); accumulate = 1: the rank's rows are added into out (in f32,
+ *   rounded once to bf16: exact over ranks that partition the vocabulary)
+ *   and the other rows are left as they are, so calling the t ranks in turn
+ *   on one buffer sums their outputs.
+ */
+tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_start,
+                             int64_t N, int64_t v_loc, int64_t h, void* out,
+                             int accumulate, void* stream);
+
+/*
+ * Its backward: dE_i f32 [v_loc, h], row v = the sum of dY[n] over the tokens
+ * n whose id is vocab_start + v, added in token order (deterministic); rows
+ * no token uses are zero. dY f32 [N, h]. h <= 16384 (else UNSUPPORTED).
+ */
+tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_start,
+                             int64_t N, int64_t v_loc, int64_t h, float* dE_i,
+                             void* stream);
+
+/*
  * Shard arithmetic of a tensor over a device mesh ([SB6] §6.1): host only,
  * no device work. A[I_{XY}, J] splits dim I over mesh axes X and Y (divided
  * by their product); axes no dim uses replicate the shard.

@@ -63,6 +63,8 @@ def load():
         "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
         "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
         "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], ctypes.c_int),
+        "tp_vocab_embed_fwd": ([vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp], ctypes.c_int),
+        "tp_vocab_embed_bwd": ([vp, vp, i64, i64, i64, i64, vp, vp], ctypes.c_int),
         "tp_row_linear_partial_chunked": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, i32,
                                            ctypes.POINTER(vp), vp], ctypes.c_int),
         "tp_vocab_ce_fwd": ([vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp], ctypes.c_int),
@@ -351,6 +353,33 @@ def tp_vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss, dZ=None, dX_part=
                                h, v_loc, _ptr(dZ), _ptr(dX_part), _ptr(dW_i), int(bool(accumulate)),
                                _stream(stream)))
     return dZ, dX_part, dW_i
+
+
+def tp_vocab_embed_fwd(ids, E_i, vocab_start, out=None, accumulate=False, stream=None):
+    """Masked lookup of this rank's table rows; returns out bf16 [N, h]."""
+    lib = load()
+    N = ids.shape[0]
+    v_loc, h = E_i.shape
+    _dev(ids, "ids", torch.int32, (N,))
+    _dev(E_i, "E_i", _bf16, (v_loc, h))
+    if out is None:
+        out = (torch.zeros if accumulate else torch.empty)((N, h), dtype=_bf16, device=E_i.device)
+    else:
+        _dev(out, "out", _bf16, (N, h))
+    _check(lib.tp_vocab_embed_fwd(_ptr(ids), _ptr(E_i), vocab_start, N, v_loc, h, _ptr(out),
+                                  int(bool(accumulate)), _stream(stream)))
+    return out
+
+
+def tp_vocab_embed_bwd(ids, dY, vocab_start, v_loc, dE_i=None, stream=None):
+    """Gradient of this rank's table rows; returns dE_i f32 [v_loc, h]."""
+    lib = load()
+    N, h = dY.shape
+    _dev(ids, "ids", torch.int32, (N,))
+    _dev(dY, "dY", _f32, (N, h))
+    dE_i = _out(dE_i, "dE_i", _f32, (v_loc, h), dY)
+    _check(lib.tp_vocab_embed_bwd(_ptr(ids), _ptr(dY), vocab_start, N, v_loc, h, _ptr(dE_i), _stream(stream)))
+    return dE_i
 
 
 def tp_shard_shape(shape, elem_bytes, axis_sizes, dim_axis_mask):

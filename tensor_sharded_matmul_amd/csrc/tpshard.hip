@@ -444,6 +444,104 @@ __global__ void __launch_bounds__(256) ce_combine_kernel(const float* __restrict
     }
 }
 
+// Vocab-parallel embedding, forward: one workgroup per token. A token whose
+// id is in this rank's rows gets its row (16-byte chunks; with accumulate
+// the row is added to the output in f32 and rounded to bf16, exact when the
+// output holds the zero row of another rank); any other token gets a zero
+// row (left as it is with accumulate).
+__global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restrict__ ids,
+                                                        const uint16_t* __restrict__ E, int64_t vocab_start,
+                                                        int v_loc, int h, uint16_t* __restrict__ out,
+                                                        int accumulate) {
+    const int64_t n = blockIdx.x;
+    const int64_t v = (int64_t)ids[n] - vocab_start;
+    const bool inside = v >= 0 && v < v_loc;
+    if (!inside && accumulate) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(E + (inside ? v : 0) * h);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + n * h);
+    for (int c = threadIdx.x; c < h / 8; c += 256) {
+        if (!inside) {
+            dst[c] = u32x4_t{0u, 0u, 0u, 0u};
+        } else if (!accumulate) {
+            dst[c] = src[c];
+        } else {
+            const u32x4_t a = src[c], b = dst[c];
+            u32x4_t r;
+            for (int k = 0; k < 4; ++k) {
+                const float lo = bf16_bits_to_f32(a[k] & 0xffffu) + bf16_bits_to_f32(b[k] & 0xffffu);
+                const float hi = bf16_bits_to_f32(a[k] >> 16) + bf16_bits_to_f32(b[k] >> 16);
+                r[k] = pack_bf16x2(lo, hi);
+            }
+            dst[c] = r;
+        }
+    }
+}
+
+// Vocab-parallel embedding, backward: one workgroup per table row v, its h
+// columns spread over the 256 threads (4 columns per thread per 1024, held
+// in registers). The ids are scanned in chunks of 256, 16 chunks of ids
+// loaded into registers at a time; a chunk's tokens whose id is
+// vocab_start + v are listed in ascending order (a wave ballot per 64 ids,
+// the four waves' matches placed by prefix counts in LDS) and their gradient
+// rows added in that order. Masks and lists alternate between two LDS
+// buffers, so a chunk without a match costs one barrier. Every row's sum is
+// taken in token order: the result does not depend on scheduling.
+constexpr int kEmbedMaxH = 16384;
+
+__global__ void __launch_bounds__(256) embed_bwd_kernel(const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ dY, int64_t vocab_start,
+                                                        int N, int h, float* __restrict__ dE) {
+    constexpr int Q = kEmbedMaxH / 1024;  // column quads per thread
+    constexpr int U = 16;                 // id chunks loaded at a time
+    __shared__ int list[2][256];
+    __shared__ uint64_t masks[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t target = vocab_start + blockIdx.x;
+    f32x4_t acc[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int chunk = 0;
+    for (int g = 0; g < N; g += 256 * U) {
+        int my[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = g + u * 256 + tid;
+            my[u] = n < N ? ids[n] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (g + u * 256 >= N) break;  // uniform
+            const int buf = chunk & 1;
+            ++chunk;
+            const bool match = my[u] >= 0 && (int64_t)my[u] == target;
+            const uint64_t mask = __ballot(match);
+            if (lane == 0) masks[buf][wave] = mask;
+            __syncthreads();
+            const int cnt = __popcll(masks[buf][0]) + __popcll(masks[buf][1]) + __popcll(masks[buf][2]) +
+                            __popcll(masks[buf][3]);
+            if (cnt == 0) continue;  // uniform
+            int before = 0;
+            for (int w = 0; w < wave; ++w) before += __popcll(masks[buf][w]);
+            if (match) list[buf][before + __popcll(mask & ((1ull << lane) - 1ull))] = g + u * 256 + tid;
+            __syncthreads();
+            for (int k = 0; k < cnt; ++k) {
+                const float* src = dY + (int64_t)list[buf][k] * h;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int c = q * 1024 + tid * 4;
+                    if (c < h) acc[q] += *reinterpret_cast<const f32x4_t*>(src + c);
+                }
+            }
+        }
+    }
+    float* row = dE + (int64_t)blockIdx.x * h;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int c = q * 1024 + tid * 4;
+        if (c < h) *reinterpret_cast<f32x4_t*>(row + c) = acc[q];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Fused-QKV regroup: a bit-exact gather of three contiguous column runs per
 // row. A workgroup moves kRegroupRows whole output rows as 16-byte chunks in
@@ -892,6 +990,50 @@ tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets
     TP_TRY((launch_gemm<false, true, EPI_CE_GRAD>(fn, a, s)));
     TP_TRY((run_gemm<false, false, EPI_F32>(fn, b, s)));
     TP_TRY((run_gemm<true, true, EPI_F32>(fn, c, s)));
+    return ok();
+}
+
+static tp_status check_embed(const char* fn, const int32_t* ids, int64_t N, int64_t v_loc, int64_t h,
+                             int64_t vocab_start) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    if (v_loc <= 0 || v_loc > 0x7fffffffLL) return fail(TP_ERR_INVALID_ARG, "%s: v_loc = %lld", fn, (long long)v_loc);
+    if (vocab_start < 0) return fail(TP_ERR_INVALID_ARG, "%s: vocab_start < 0", fn);
+    if (N > 0 && (ids == nullptr || (reinterpret_cast<uintptr_t>(ids) & 3u)))
+        return fail(TP_ERR_INVALID_ARG, "%s: ids is NULL or not 4-byte aligned", fn);
+    TP_TRY(check_elems(fn, v_loc, h));
+    TP_TRY(check_elems(fn, N, h));
+    return TP_OK;
+}
+
+tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_start, int64_t N, int64_t v_loc,
+                             int64_t h, void* out, int accumulate, void* stream) {
+    const char* fn = "tp_vocab_embed_fwd";
+    TP_TRY(check_embed(fn, ids, N, v_loc, h, vocab_start));
+    TP_CHECK_PTR(E_i, "E_i");
+    TP_CHECK_TOK_PTR(out, "out");
+    if (N == 0) return ok();
+    if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    hipLaunchKernelGGL(embed_fwd_kernel, dim3((unsigned)N), dim3(256), 0, static_cast<hipStream_t>(stream), ids,
+                       static_cast<const uint16_t*>(E_i), vocab_start, (int)v_loc, (int)h,
+                       static_cast<uint16_t*>(out), accumulate ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_start, int64_t N, int64_t v_loc,
+                             int64_t h, float* dE_i, void* stream) {
+    const char* fn = "tp_vocab_embed_bwd";
+    TP_TRY(check_embed(fn, ids, N, v_loc, h, vocab_start));
+    if (h > kEmbedMaxH) return fail(TP_ERR_UNSUPPORTED, "%s: h = %lld above %d", fn, (long long)h, kEmbedMaxH);
+    if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    TP_CHECK_TOK_PTR(dY, "dY");
+    TP_CHECK_PTR(dE_i, "dE_i");
+    hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)v_loc), dim3(256), 0, static_cast<hipStream_t>(stream), ids,
+                       dY, vocab_start, (int)N, (int)h, dE_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
 

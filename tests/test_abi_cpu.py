@@ -102,6 +102,22 @@ def test_kv_grad_accumulate_validates_before_launch():
     assert f(NULL, NULL, 0, 64, 8, 128, 16, NULL) == 0               # h = 0: nothing to do
 
 
+def test_vocab_calls_validate_before_launch():
+    fwd = _raw("tp_vocab_embed_fwd")
+    assert fwd(NULL, NULL, 0, 16, 1000, 8192, NULL, 0, NULL) == 1           # NULL ids
+    assert fwd(NULL, NULL, 0, 16, 1000, 100, NULL, 0, NULL) == 3            # h % 64
+    bwd = _raw("tp_vocab_embed_bwd")
+    odd = ctypes.c_void_p(0x1010)
+    assert bwd(odd, NULL, 0, 16, 1000, 32768, NULL, NULL) == 3              # h above the register tile
+    ce = _raw("tp_vocab_ce_fwd")
+    assert ce(NULL, NULL, NULL, 0, 16, 8192, 16128, NULL, NULL, NULL, NULL) == 1   # NULL targets
+    assert ce(NULL, NULL, odd, -1, 16, 8192, 16128, NULL, NULL, NULL, NULL) == 1   # vocab_start < 0
+    comb = _raw("tp_vocab_ce_combine")
+    assert comb(NULL, NULL, NULL, 0, 16, NULL, NULL, NULL, NULL) == 1               # t = 0
+    ch = _raw("tp_row_linear_partial_chunked")
+    assert ch(NULL, NULL, NULL, 16, 1024, 8192, 0, 0, NULL, NULL) == 1             # nchunks = 0
+
+
 def test_regroup_width_matches_oracle():
     for n_h, n_kv, d_h, t in [(64, 8, 128, 8), (64, 8, 128, 16), (32, 8, 128, 32), (64, 8, 128, 4)]:
         assert T.regroup_width(n_h, n_kv, d_h, t) == len(O.qkv_regroup_index(n_h, n_kv, d_h, t, 0))

@@ -1,0 +1,42 @@
+"""Vocab-parallel embedding through the C ABI: each rank's masked lookup is a
+bit-exact copy of the oracle's, the t ranks accumulated on one buffer give the
+full lookup (equal in value), and the table gradient equals the oracle's
+(exact on integer gradients; repeated ids summed in token order)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import tensor_sharded_matmul_amd as T
+from gpu_util import TOL, bits, err, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,V,h,t", [(300, 1000, 256, 4), (4096, 16128 * 2, 8192, 2), (5, 64, 64, 1)])
+def test_embedding_forward_backward(N, V, h, t):
+    rng = np.random.default_rng(N + V)
+    v_loc = V // t
+    E = synth.draw(rng, (V, h))
+    ids = rng.integers(0, V, size=N).astype(np.int32)
+    ids[: min(N, 4)] = [0, V - 1, v_loc - 1, v_loc][: min(N, 4)]
+    ids[N // 2:] = ids[: N - N // 2]                 # repeated ids
+    idd = torch.from_numpy(ids).to("cuda:0")
+    acc = torch.zeros((N, h), dtype=torch.bfloat16, device="cuda:0")
+    for i in range(t):
+        Ei = E[i * v_loc:(i + 1) * v_loc]
+        out = T.tp_vocab_embed_fwd(idd, to_dev(Ei), i * v_loc)
+        T.tp_vocab_embed_fwd(idd, to_dev(Ei), i * v_loc, out=acc, accumulate=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), O.vocab_embed_fwd(ids, Ei, i * v_loc))
+    # the sum over ranks equals the full lookup in value (a -0.0 entry of the
+    # table plus the other ranks' +0.0 is +0.0, as any summing exchange gives)
+    assert np.array_equal(f64(acc), synth.bf16_to_f64(E[ids]))
+
+    dY = synth.bf16_to_f64(synth.int_inputs(90, (N, h))).astype(np.float32)   # exact sums
+    dYd = torch.from_numpy(dY).to("cuda:0")
+    for i in range(t):
+        dE = T.tp_vocab_embed_bwd(idd, dYd, i * v_loc, v_loc)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(dE), O.vocab_embed_bwd(ids, dY, i * v_loc, v_loc)), i
