@@ -133,18 +133,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// erf from Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for x >= 0, erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// exp(-x^2) with t = 1 / (1 + p x), absolute error at most 1.5e-7 (far below
+// the 2^-9 relative rounding of the bf16 outputs); odd in x. Straight-line
+// code: one reciprocal, one exponential, five multiply-adds.
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    return copysignf(1.0f - poly * __expf(-ax * ax), x);
+}
+
 __device__ __forceinline__ float gelu_f(float x) {
-    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f));
 }
 
 __device__ __forceinline__ float gelu_grad_f(float x) {
-    const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+    const float cdf = 0.5f * (1.0f + erf_as(x * 0.70710678118654752f));
     const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
     return cdf + x * pdf;
 }
 
+// 1 / (1 + e^-x) with the hardware reciprocal (1 ulp) instead of a division
 __device__ __forceinline__ float sigmoid_f(float x) {
-    return 1.0f / (1.0f + __expf(-x));
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // ---------------------------------------------------------------------------
