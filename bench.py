@@ -287,7 +287,7 @@ def main() -> int:
     # GEMM2 computed in token-row chunks with an event per chunk (the schedule
     # that lets the exchange of chunk c overlap chunk c + 1): its overhead
     chunked = {}
-    for nc in (2, 4, 8):
+    for nc in (() if args.no_rows else (2, 4, 8)):
         evs = [torch.cuda.Event() for _ in range(nc)]
 
         def g2c():
@@ -296,7 +296,8 @@ def main() -> int:
         ms_c = time_fn(g2c, args.reps)[0]
         chunked[str(nc)] = {"ms": round(ms_c, 4), "tflops": round(fl["gemm2_down_partial"] / (ms_c * 1e-3) / 1e12, 1),
                             "overhead": round(ms_c / kt["gemm2_down_partial"]["ms"] - 1, 3)}
-    kt["gemm2_down_partial_chunked"] = chunked
+    if chunked:
+        kt["gemm2_down_partial_chunked"] = chunked
 
     rows = {"mlp_kernels": kt,
             "fwd_ms": round(time_fn(fwd, args.reps)[0], 4), "bwd_ms": round(bwd_mean, 4)}
