@@ -131,6 +131,14 @@ static tp_status workspace(const char* fn, hipStream_t s, size_t bytes, float** 
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto& w = g_ws[{dev, s}];
     if (w.second < bytes) {
+        // growing needs a stream synchronisation and hipMalloc, neither of
+        // which a stream under graph capture allows
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+            return fail(TP_ERR_INVALID_ARG,
+                        "%s: the workspace of this stream must grow to %zu bytes while the stream is being "
+                        "captured; run the call once on the stream before capturing it",
+                        fn, bytes);
         if (w.first) {
             // earlier work on this stream may still read the old buffer
             e = hipStreamSynchronize(s);

@@ -167,3 +167,29 @@ def test_empty_token_count_is_a_noop():
     P = T.tp_row_linear_partial(Z, W)
     torch.cuda.synchronize()
     assert P.shape == (0, 64)
+
+
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        N = int(rng.choice([1, 7, 16, 33, 64, 100, 255, 256, 257, 700, 1500]))
+        k = 64 * int(rng.integers(1, 40))
+        n = 64 * int(rng.integers(1, 40))
+        out.append((N, k, n))
+    return out
+
+
+@pytest.mark.parametrize("N,k,n", _random_shapes(2024, 12))
+def test_random_shapes_every_layout_exact(N, k, n):
+    # seeded random shapes: NN (forward, incl. split-K and decode tiles), NT and TN
+    Xb, X = _ints(100, (N, k))
+    Wb, W = _ints(101, (k, n))
+    dYb, dY = _ints(102, (N, n))
+    P = T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb))
+    dX, dW = T.tp_col_linear_bwd(to_dev(Xb), to_dev(Wb), to_dev(dYb))
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(P), O.row_linear_partial(X, W))
+    want_dx, want_dw = O.col_linear_bwd(X, W, dY)
+    assert np.array_equal(f64(dX), want_dx)
+    assert np.array_equal(f64(dW), want_dw)

@@ -73,3 +73,24 @@ def test_graph_replays_match_eager():
         want = O.col_linear(f64(X), f64(W))
         assert err(f64(Y), want) <= TOL
     del graph
+
+
+def test_capture_before_the_workspace_exists_is_refused():
+    # a stream whose split-K workspace does not exist yet cannot create it
+    # while it is captured: the call reports it and enqueues nothing
+    N, h, n = 16, 2048, 384
+    X = to_dev(_normal(60, (N, h)))
+    W = to_dev(_normal(61, (h, n), h))
+    Y = torch.empty((N, n), dtype=torch.bfloat16, device="cuda:0")
+    fresh = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(ValueError, match="captured"):
+        with torch.cuda.graph(graph, stream=fresh):
+            T.tp_col_linear(X, W, "none", Y=Y)
+    torch.cuda.synchronize()
+    # the same call outside capture works, after which capture does too
+    with torch.cuda.stream(fresh):
+        T.tp_col_linear(X, W, "none", Y=Y)
+    torch.cuda.synchronize()
+    want = O.col_linear(f64(X), f64(W))
+    assert err(f64(Y), want) <= TOL
