@@ -42,8 +42,8 @@ KERNEL_DESC = {
     "gemm1_gate_up_swiglu": "gemm_kernel NN, 256x224 tile (112 gate + 112 up columns), SwiGLU epilogue",
     "gemm2_down_partial": "gemm_kernel NN, 256x256 tile, fp32 store",
     "bwd_dx_partial": "gemm_kernel NT, 256x256 tile, fp32 store",
-    "bwd_dw_gate_up": "gemm_kernel TN, 256x224 tile, fp32 store",
-    "bwd_dw_down": "gemm_kernel TN, 224x256 tile, fp32 store",
+    "bwd_dw_gate_up": "gemm_kernel TN, 256x224 tile, 8 waves, fp32 store",
+    "bwd_dw_down": "gemm_kernel TN, 224x256 tile, 8 waves, fp32 store",
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic_dominant_kernel.json")
 
