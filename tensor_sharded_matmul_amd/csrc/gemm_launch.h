@@ -94,11 +94,12 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
     constexpr bool SW = (EPI == EPI_SWIGLU);
     // Weight-gradient (TN) products run 8 waves, two per SIMD (128 x 64 or
     // 64 x 112 accumulator blocks): their two transposing LDS reads per
-    // fragment leave gaps the second wave fills (+2 % measured; the NN and
-    // NT products are as fast or faster with 4 waves).
+    // fragment leave gaps the second wave fills (+2 % measured). So does the
+    // NT 256 x 224 tile (the SwiGLU' dZ product: +4 %); the other NN and NT
+    // tiles are as fast or faster with 4 waves.
     constexpr int WM_SQ = 2, WN_SQ = A_T ? 4 : 2;
     using Sq = CfgOf<A_T, B_KN, 256, 256, 256, 256, WM_SQ, WN_SQ>;
-    using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, A_T ? 4 : 2, 2>;
+    using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, (A_T || !B_KN) ? 4 : 2, 2>;
     using M224 = CfgOf<A_T, B_KN, 256, 256, 224, 256, 2, A_T ? 4 : 2>;
     using SwiN224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 4, 1>;  // SwiGLU: 112 gate + 112 up columns
     if constexpr (!A_T && B_KN && EPI == EPI_F32) {
