@@ -23,16 +23,21 @@
  *   Pointers:  device pointers (hipMalloc'd or torch CUDA tensors), 16-byte
  *              aligned. The caller owns every buffer; the library keeps no
  *              pointer to them after the call returns.
- *   Workspace: the forward GEMMs of tp_col_linear, tp_row_linear_partial and
- *              tp_mlp_shard_fwd at N <= 64 tokens split K over workgroups and
- *              sum the f32 partials in a second kernel. Their scratch is one
- *              device buffer per (device, stream) that the library allocates
- *              on first use, grows when a larger one is needed (after
- *              synchronising that stream) and keeps until the process ends:
- *              at most 4 * min(4 * CUs / tiles, k / 128) * N * n f32 bytes,
- *              a few MB for model widths. Every other call allocates
- *              nothing. Calls that overlap on one stream cannot race on it;
- *              a failed allocation returns TP_ERR_HIP with nothing enqueued.
+ *   Workspace: a product with too few output tiles for the CUs (N <= 64
+ *              tokens, or a narrow shard such as the attention projections')
+ *              splits K over workgroups and sums the f32 partials in a
+ *              second kernel; tp_vocab_ce_fwd keeps per-tile records. Their
+ *              scratch is one device buffer per (device, stream) that the
+ *              library allocates on first use, grows when a larger one is
+ *              needed (after synchronising that stream) and keeps until the
+ *              process ends: ksplit * N * n * 4 bytes for a split product
+ *              (a few MB at decode sizes, up to ~70 MB for the Llama-3-70B
+ *              attention shards). No call allocates anything else. Calls on
+ *              one stream are ordered, so they cannot race on it. A call
+ *              reserves what it needs before it enqueues anything: a failed
+ *              allocation returns TP_ERR_HIP, and growing it while the
+ *              stream is being captured into a graph returns
+ *              TP_ERR_INVALID_ARG (run the call once on that stream first).
  *   Sizes:     N (tokens) is any value >= 0 (N = 0 is a no-op). Model widths
  *              (k, n, h, f, k_loc) must be positive multiples of 64.
  *   Streams:   `stream` is a hipStream_t (NULL = the legacy default stream).
