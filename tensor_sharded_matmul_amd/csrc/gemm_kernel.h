@@ -10,8 +10,9 @@
 // ([TPSP] "MLP：先列后行": GeLU and SiLU(gate)*up are local, per element).
 //
 // Design (gfx950 / CDNA4):
-//  * WAVES_M x WAVES_N waves of 64 lanes, one workgroup per CU. Each wave owns
-//    a (TM/WAVES_M) x (TN/WAVES_N) sub-tile of C in f32 accumulators (AGPRs).
+//  * WAVES_M x WAVES_N waves of 64 lanes (4, or 8 = two per SIMD), one
+//    workgroup per CU. Each wave owns a (TM/WAVES_M) x (TN/WAVES_N) sub-tile
+//    of C in f32 accumulators (AGPRs).
 //  * v_mfma_f32_16x16x32_bf16 with the operands swapped (the MFMA "A" operand
 //    is the B tile), so each lane ends with 4 consecutive columns of one C row
 //    and epilogue stores are 16-byte (f32) or 8-byte (bf16) vectors.
@@ -23,9 +24,9 @@
 //    drain every LDS-DMA load before each barrier). Rows past K (and past
 //    M / N) read as zero through the buffer descriptor's range check.
 //  * Fragments are double-buffered in registers: the LDS reads of k-step
-//    kt+1 are interleaved with the MFMAs of k-step kt (pinned with
-//    sched_group_barrier), so with one wave per SIMD the matrix core does not
-//    wait on LDS latency; one barrier per k-step.
+//    kt+1 are interleaved with the MFMAs of k-step kt (at issue slots fixed
+//    at compile time and pinned with sched_barrier fences), so the matrix
+//    core does not wait on LDS latency; one barrier per k-step.
 //  * The loaded tile (BM x BN) may be wider than the computed one (TM x TN):
 //    224-wide computed tiles divide the 3584 / 7168 widths of the Llama-3-70B
 //    shard into a whole number of waves of 256 workgroups, while loads stay in

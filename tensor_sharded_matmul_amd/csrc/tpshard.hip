@@ -113,11 +113,13 @@ static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, i
 }
 
 // ---------------------------------------------------------------------------
-// Split-K for products with few token rows (decode). A forward product with
-// M <= 64 rows has too few output tiles to keep 256 CUs streaming its weight
-// from HBM, so K is split over workgroups: each writes an fp32 partial of the
-// whole [M, n_w] product to a workspace, and splitk_reduce sums the partials
-// and applies the epilogue (store, accumulate, GeLU, SwiGLU).
+// Split-K. A product with too few output tiles for the CUs (decode-sized
+// token counts, or the narrow attention shards) has K split over workgroups:
+// each writes an fp32 partial of the whole product to a workspace, and
+// splitk_reduce sums the partials in split order and applies the epilogue
+// (store, accumulate, GeLU, SwiGLU). (Summing in the GEMM kernel by the last
+// workgroup of a tile needs device-scope fences, which write back and
+// invalidate each XCD's L2 for every workgroup: measured 1.5-3x slower.)
 // The workspace belongs to the library: one buffer per (device, stream),
 // grown on demand (hipMalloc outside any kernel; kept until the process
 // ends), so calls on different streams never share one.
