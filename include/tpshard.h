@@ -38,8 +38,11 @@
  *              allocation returns TP_ERR_HIP, and growing it while the
  *              stream is being captured into a graph returns
  *              TP_ERR_INVALID_ARG (run the call once on that stream first).
- *   Sizes:     N (tokens) is any value >= 0 (N = 0 is a no-op). Model widths
- *              (k, n, h, f, k_loc) must be positive multiples of 64.
+ *   Sizes:     N (tokens) is any value from 0 to 2^30 (N = 0 is a no-op).
+ *              Model widths (k, n, h, f, k_loc; the LM head's v_loc) must be positive
+ *              multiples of 64 and at most 2^20 (larger: UNSUPPORTED). No
+ *              limit on a buffer's size: operands and outputs above 4 GiB
+ *              are addressed like small ones.
  *   Streams:   `stream` is a hipStream_t (NULL = the legacy default stream).
  *              Work is enqueued asynchronously; no host synchronisation.
  *              Faults in kernels surface at the caller's next synchronisation.

@@ -178,3 +178,14 @@ def int_inputs(seed: int, shape, lo: int = -2, hi: int = 2) -> np.ndarray:
     rng = np.random.default_rng(seed)
     x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
     return bf16_round(x)
+
+
+def int_inputs_device(seed: int, shape, device, lo: int = -3, hi: int = 3):
+    """Small integers in [lo, hi] as a bf16 torch tensor drawn on `device` by
+    torch's seeded generator: inputs of several GiB that a host draw would take
+    minutes to produce. Host checks copy the rows or columns they need."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randint(lo, hi + 1, tuple(shape), generator=g, device=device, dtype=torch.int8)
+    return x.to(torch.bfloat16)

@@ -98,7 +98,7 @@ struct GemmArgs {
     int ldc, ldc2;   // leading dims of C and C2 / aux (elements)
     int f;           // SWIGLU / SWIGLU_BWD: column offset of the "up" half
     int accumulate;  // EPI_F32: add into C
-    uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (buffer range check)
+    uint64_t a_bytes, b_bytes;  // extent of A and B in bytes (buffer range check)
     // Split-K: ksplit workgroups per output tile, each contracting kper rows
     // of K (a multiple of 64; the last split ends at K); split s writes its
     // fp32 partial to C + s * M * ldc. ksplit = 1: the whole K, C as given.
@@ -175,6 +175,64 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
     r[3] = 0x00020000;                                // gfx9 data format word
     return r;
 }
+
+// Descriptor of the part of an operand that starts `off` bytes into its
+// `total`-byte extent: 64-bit base, so that the 32-bit per-lane offsets only
+// span one tile (K-contiguous operands) or one stage (MN-contiguous ones)
+// whatever the operand's size; the range checked is what remains of the
+// extent, clamped to 32 bits (no offset reaches the clamp).
+__device__ __forceinline__ i32x4_t window_rsrc(const uint16_t* base, uint64_t total, uint64_t off) {
+    const uint64_t rest = off < total ? total - off : 0;
+    return make_rsrc(reinterpret_cast<const uint8_t*>(base) + off,
+                     rest > 0xffffffffull ? 0xffffffffu : (uint32_t)rest);
+}
+
+// The stage of an operand that is loaded next, and how to move to the one
+// after it. Normally the descriptor stays and the per-lane k offset moves by
+// a stage (k-rows x 2 bytes, K-contiguous; k-rows x pitch x 2 bytes,
+// MN-contiguous). An MN-contiguous operand whose window spans 2^31 bytes or
+// more (MOVE_BASE: K x pitch that large) instead moves the descriptor's base
+// by a stage and shrinks the remaining extent, saturating at 0: scalar
+// instructions only, issued right after the stage's last load, in the
+// shadow of the MFMAs (about 1.5 % of the product's time, which is why it is
+// not the default).
+template <bool MOVE_BASE>
+struct StageCursor {
+    i32x4_t rs;          // descriptor of the next stage
+    uint32_t ko;         // its per-lane k offset (K-contiguous operand)
+    uint32_t step_lo, step_hi;
+    uint64_t base;       // MN: first byte of the next stage
+    uint32_t rest_lo, rest_hi;  // MN: bytes of the extent from base on
+
+    __device__ __forceinline__ void init(const uint16_t* p, uint64_t total, uint64_t org, uint64_t step) {
+        rs = window_rsrc(p, total, org);
+        ko = 0;
+        step_lo = (uint32_t)step;
+        step_hi = (uint32_t)(step >> 32);
+        base = reinterpret_cast<uint64_t>(p) + org;
+        const uint64_t rest = org < total ? total - org : 0;
+        rest_lo = (uint32_t)rest;
+        rest_hi = (uint32_t)(rest >> 32);
+    }
+    __device__ __forceinline__ void next() {
+        if constexpr (MOVE_BASE) {
+            base += ((uint64_t)step_hi << 32) | step_lo;
+            asm volatile(
+                "s_sub_u32 %0, %0, %2\n\t"
+                "s_subb_u32 %1, %1, %3\n\t"
+                "s_cselect_b32 %0, 0, %0\n\t"
+                "s_cselect_b32 %1, 0, %1"
+                : "+s"(rest_lo), "+s"(rest_hi)
+                : "s"(step_lo), "s"(step_hi)
+                : "scc");
+            rs[0] = (int32_t)(uint32_t)base;
+            rs[1] = (int32_t)((uint32_t)(base >> 32) & 0xffffu);
+            rs[2] = (int32_t)(rest_hi != 0 ? 0xffffffffu : rest_lo);
+        } else {
+            ko += step_lo;
+        }
+    }
+};
 
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
@@ -656,7 +714,7 @@ struct RingModel {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <class CF, bool A_T, bool B_KN, int EPI>
+template <class CF, bool A_T, bool B_KN, int EPI, bool WIDE>
 __global__ void __launch_bounds__(64 * CF::WAVES_M * CF::WAVES_N)
 gemm_kernel(const GemmArgs args) {
     constexpr int BM = CF::BM, BN = CF::BN, TM = CF::TM, TN = CF::TN;
@@ -703,12 +761,13 @@ gemm_kernel(const GemmArgs args) {
     // --- this workgroup's K range (split-K) ---
     const int k0 = split * args.kper;
     const int Kloc = args.ksplit > 1 ? min(args.K, k0 + args.kper) - k0 : args.K;
-    const uint32_t a_k0 = (uint32_t)k0 * (A_T ? (uint32_t)args.lda : 1u) * 2u;  // bytes
-    const uint32_t b_k0 = (uint32_t)k0 * (B_KN ? (uint32_t)args.ldb : 1u) * 2u;
-
     // --- DMA descriptors and per-lane offsets ---
-    const i32x4_t rsA = make_rsrc(reinterpret_cast<const uint8_t*>(args.A) + a_k0, args.a_bytes - a_k0);
-    const i32x4_t rsB = make_rsrc(reinterpret_cast<const uint8_t*>(args.B) + b_k0, args.b_bytes - b_k0);
+    // The window of an operand starts at this workgroup's first k-row (and,
+    // K-contiguous, at its tile's first row): byte offset org.
+    const uint64_t a_org = (uint64_t)k0 * (A_T ? (uint64_t)args.lda : 1u) * 2u +
+                           (A_T ? 0u : (uint64_t)m0 * (uint64_t)args.lda * 2u);
+    const uint64_t b_org = (uint64_t)k0 * (B_KN ? (uint64_t)args.ldb : 1u) * 2u +
+                           (B_KN ? 0u : (uint64_t)n0 * (uint64_t)args.ldb * 2u);
     using ADma = typename std::conditional<A_T, MNTileDma<BM, BKA, NWAVES>, KTileDma<BM, BKA, NWAVES>>::type;
     using BDma = typename std::conditional<B_KN, MNTileDma<BN, BKB, NWAVES>, KTileDma<BN, BKB, NWAVES>>::type;
     ADma da;
@@ -716,7 +775,7 @@ gemm_kernel(const GemmArgs args) {
     if constexpr (A_T) {
         da.init(wave, lane, args.lda, IdentityCols{m0, args.M});
     } else {
-        da.init(wave, lane, m0, args.lda);
+        da.init(wave, lane, 0, args.lda);
     }
     if constexpr (B_KN) {
         if constexpr (SWIGLU) {
@@ -725,21 +784,23 @@ gemm_kernel(const GemmArgs args) {
             db.init(wave, lane, args.ldb, IdentityCols{n0, args.N});
         }
     } else {
-        db.init(wave, lane, n0, args.ldb);
+        db.init(wave, lane, 0, args.ldb);
     }
-    const uint32_t a_step = A_T ? (uint32_t)BKA * (uint32_t)args.lda * 2u : (uint32_t)BKA * 2u;
-    const uint32_t b_step = B_KN ? (uint32_t)BKB * (uint32_t)args.ldb * 2u : (uint32_t)BKB * 2u;
+    StageCursor<A_T && WIDE> ca;
+    StageCursor<B_KN && WIDE> cb;
+    ca.init(args.A, args.a_bytes, a_org, A_T ? (uint64_t)BKA * (uint64_t)args.lda * 2u : (uint64_t)BKA * 2u);
+    cb.init(args.B, args.b_bytes, b_org, B_KN ? (uint64_t)BKB * (uint64_t)args.ldb * 2u : (uint64_t)BKB * 2u);
     const uint32_t ldsA = lds_addr(smem), ldsB = ldsA + SA * A_STAGE;
     constexpr int LA = ADma::kPerWave, LB = BDma::kPerWave;  // loads per stage per wave
     constexpr RingModel ring{PA, SA, LA, PB, SB, LB};
 
     // load d of this wave's share of a stage of operand A / B: LDS buffer at
-    // byte offset `buf` of the ring, k-rows starting at byte offset `kb`
-    auto issue_a = [&](auto dc, uint32_t buf, uint32_t kb) {
-        da.issue_one(decltype(dc)::value, rsA, ldsA + buf, wave, kb);
+    // byte offset `buf` of the ring, the stage's descriptor and k offset
+    auto issue_a = [&](auto dc, uint32_t buf, i32x4_t rs, uint32_t ko) {
+        da.issue_one(decltype(dc)::value, rs, ldsA + buf, wave, ko);
     };
-    auto issue_b = [&](auto dc, uint32_t buf, uint32_t kb) {
-        db.issue_one(decltype(dc)::value, rsB, ldsB + buf, wave, kb);
+    auto issue_b = [&](auto dc, uint32_t buf, i32x4_t rs, uint32_t ko) {
+        db.issue_one(decltype(dc)::value, rs, ldsB + buf, wave, ko);
     };
 
     // --- fragment addresses in buffer 0 of each ring ---
@@ -833,7 +894,6 @@ gemm_kernel(const GemmArgs args) {
     // compare-and-wrap, no division): the buffer the next fragment reads
     // come from, the buffer the next load goes to, and that load's k offset.
     uint32_t a_rd = 0, b_rd = 0, a_wr = 0, b_wr = 0;
-    uint32_t a_kb = (uint32_t)SA * a_step, b_kb = (uint32_t)SB * b_step;
     auto wrap_a = [](uint32_t x) { x += A_STAGE; return x == (uint32_t)(SA * A_STAGE) ? 0u : x; };
     auto wrap_b = [](uint32_t x) { x += B_STAGE; return x == (uint32_t)(SB * B_STAGE) ? 0u : x; };
 
@@ -858,7 +918,9 @@ gemm_kernel(const GemmArgs args) {
         }
         if constexpr (IA) a_rd = wrap_a(a_rd);
         if constexpr (IB) b_rd = wrap_b(b_rd);
-        const uint32_t soa = a_rd, sob = b_rd, wa = a_wr, wb = b_wr, ka = a_kb, kb = b_kb;
+        const uint32_t soa = a_rd, sob = b_rd, wa = a_wr, wb = b_wr;
+        const i32x4_t ra = ca.rs, rb = cb.rs;
+        const uint32_t ka = ca.ko, kb = cb.ko;
         static_for<0, NMFMA>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             mfma_one(cur, mc);
@@ -868,8 +930,15 @@ gemm_kernel(const GemmArgs args) {
                 if constexpr (k < SL::begin(m + 1) && k < SL::NOPS) {
                     if constexpr (SL::is_load(k)) {
                         constexpr int d = SL::loads_before(k);
-                        if constexpr (d < NDA) issue_a(std::integral_constant<int, d>{}, wa, ka);
-                        else issue_b(std::integral_constant<int, d - NDA>{}, wb, kb);
+                        // after a stage's last load, its cursor moves on
+                        // (scalar work in the shadow of the MFMAs)
+                        if constexpr (d < NDA) {
+                            issue_a(std::integral_constant<int, d>{}, wa, ra, ka);
+                            if constexpr (d == NDA - 1) ca.next();
+                        } else {
+                            issue_b(std::integral_constant<int, d - NDA>{}, wb, rb, kb);
+                            if constexpr (d == NDMA - 1) cb.next();
+                        }
                     } else {
                         read_one(nxt, std::integral_constant<int, k - SL::loads_before(k)>{}, soa, sob,
                                  std::integral_constant<int, HA>{}, std::integral_constant<int, HB>{});
@@ -878,8 +947,8 @@ gemm_kernel(const GemmArgs args) {
                 }
             });
         });
-        if constexpr (IA) { a_wr = wrap_a(a_wr); a_kb += a_step; }
-        if constexpr (IB) { b_wr = wrap_b(b_wr); b_kb += b_step; }
+        if constexpr (IA) a_wr = wrap_a(a_wr);
+        if constexpr (IB) b_wr = wrap_b(b_wr);
     };
 
     if (U > 0) {  // K = 0 (no tokens in a weight gradient): C = 0
@@ -896,10 +965,13 @@ gemm_kernel(const GemmArgs args) {
                 constexpr int pp = o == 0 ? PA : PB, SS = o == 0 ? SA : SB;
                 if constexpr ((t + 1) % pp == 0 && (t + 1) / pp + SS - 1 >= 0) {
                     constexpr int st = (t + 1) / pp + SS - 1;
-                    if constexpr (o == 0)
-                        static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), (uint32_t)st * a_step); });
-                    else
-                        static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), (uint32_t)st * b_step); });
+                    if constexpr (o == 0) {
+                        static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), ca.rs, ca.ko); });
+                        ca.next();
+                    } else {
+                        static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), cb.rs, cb.ko); });
+                        cb.next();
+                    }
                 }
             }
         });

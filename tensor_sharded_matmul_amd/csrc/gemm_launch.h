@@ -14,14 +14,28 @@ namespace tps {
 // Records a formatted message for tp_last_error and returns st.
 tp_status fail(tp_status st, const char* fmt, ...);
 
+// Does an MN-contiguous operand's window (its K rows plus the stages loaded
+// past the end, times its pitch) reach 2^31 bytes? Then the kernel moves its
+// descriptor along K (the WIDE variant).
+inline bool mn_window_wide(bool mn, int64_t K, int64_t ld) {
+    return mn && (K + 512) * ld * 2 >= ((int64_t)1 << 31);
+}
+
 template <class CF, bool A_T, bool B_KN, int EPI>
 inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
     constexpr int TNZ = (EPI == EPI_SWIGLU) ? CF::TN / 2 : CF::TN;
     const long long tiles = (long long)((a.M + CF::TM - 1) / CF::TM) * ((a.N + TNZ - 1) / TNZ) * a.ksplit;
     if (tiles == 0) return TP_OK;
     if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-    hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI>), dim3((unsigned)tiles),
-                       dim3(64 * CF::WAVES_M * CF::WAVES_N), 0, s, a);
+    const dim3 grid((unsigned)tiles), block(64 * CF::WAVES_M * CF::WAVES_N);
+    bool wide = false;
+    if constexpr (A_T || B_KN)
+        wide = mn_window_wide(A_T, a.K, a.lda) || mn_window_wide(B_KN, a.K, a.ldb);
+    if (wide) {
+        if constexpr (A_T || B_KN) hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI, true>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI, false>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return TP_OK;
@@ -31,8 +45,13 @@ inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
 #define TPS_DEC_SB 8  // stages of the weight ring of the decode tiles
 #endif
 
-// Operands are addressed with 32-bit byte offsets (buffer descriptors).
-static constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
+// Operands of any size are addressed from 64-bit descriptor bases (a tile's
+// first row; a workgroup's first k-row). The 32-bit per-lane offsets then
+// span one tile of a K-contiguous operand (256 rows of its pitch) or one
+// stage of an MN-contiguous one (the WIDE variant) or its whole window, which
+// bounds the pitches (elements) so that every offset stays below 2^31.
+static constexpr int64_t kMaxKPitch = (int64_t)1 << 21;
+static constexpr int64_t kMaxMNPitch = (int64_t)1 << 23;
 
 // Compute units of the current device (cached per device; tpshard.hip).
 int device_cus();
@@ -132,12 +151,10 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
 template <bool A_T, bool B_KN, int EPI>
 tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
     if (a.M == 0 || a.N == 0) return TP_OK;
-    const int64_t a_bytes = (int64_t)(A_T ? a.K : a.M) * a.lda * 2;
-    const int64_t b_bytes = (int64_t)(B_KN ? a.K : a.N) * a.ldb * 2;
-    if (a_bytes > kMaxOperandBytes || b_bytes > kMaxOperandBytes)
-        return fail(TP_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
-    a.a_bytes = (uint32_t)a_bytes;
-    a.b_bytes = (uint32_t)b_bytes;
+    if (a.lda > (A_T ? kMaxMNPitch : kMaxKPitch) || a.ldb > (B_KN ? kMaxMNPitch : kMaxKPitch))
+        return fail(TP_ERR_UNSUPPORTED, "%s: an operand's row pitch is too large", fn);
+    a.a_bytes = (uint64_t)(A_T ? a.K : a.M) * (uint64_t)a.lda * 2u;
+    a.b_bytes = (uint64_t)(B_KN ? a.K : a.N) * (uint64_t)a.ldb * 2u;
     if constexpr (EPI == EPI_CE_STATS) {
         using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
         // one record per row for each 112-column wave block of 256 x 224

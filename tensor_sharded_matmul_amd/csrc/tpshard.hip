@@ -65,11 +65,15 @@ static tp_status check_tokens(const char* fn, int64_t N) {
     return TP_OK;
 }
 
+// Widths become the row pitches of the GEMM operands (a SwiGLU weight's is
+// twice its width); 2^20 keeps every pitch inside the kernel's limits.
+static constexpr int64_t kMaxWidth = (int64_t)1 << 20;
+
 static tp_status check_width(const char* fn, const char* name, int64_t v) {
     if (v <= 0) return fail(TP_ERR_INVALID_ARG, "%s: %s = %lld must be positive", fn, name, (long long)v);
     if (v % 64 != 0)
         return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld is not a multiple of 64", fn, name, (long long)v);
-    if (v > (int64_t)1 << 24) return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld too large", fn, name, (long long)v);
+    if (v > kMaxWidth) return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld too large", fn, name, (long long)v);
     return TP_OK;
 }
 

@@ -127,6 +127,9 @@ def test_gemm_entry_points_validate_before_launch():
     col = _raw("tp_col_linear")
     assert col(NULL, NULL, NULL, 16, 8192, 1280, 0, NULL, NULL) == 1          # NULL X
     assert col(NULL, NULL, NULL, 16, 100, 1280, 0, NULL, NULL) == 3           # k % 64
+    assert col(NULL, NULL, NULL, 16, (1 << 20) + 64, 1280, 0, NULL, NULL) == 3  # k above 2^20
+    assert "too large" in T.tp_last_error()
+    assert col(NULL, NULL, NULL, (1 << 30) + 1, 8192, 1280, 0, NULL, NULL) == 3  # N above 2^30
     assert col(NULL, NULL, NULL, -1, 8192, 1280, 0, NULL, NULL) == 1          # N < 0
     assert col(NULL, NULL, NULL, 16, 8192, 1280, 7, NULL, NULL) == 1          # act
     odd = ctypes.c_void_p(0x1008)
