@@ -49,7 +49,12 @@
  *   Errors:    arguments are validated before any launch; on failure nothing
  *              is enqueued, a status != TP_OK is returned and a message is
  *              kept in thread-local storage (tp_last_error). Calls are
- *              re-entrant across threads and streams.
+ *              re-entrant across threads as long as each stream is used by
+ *              one host thread at a time (a stream's workspace may be
+ *              replaced by a call on it while another thread still
+ *              enqueues work that uses the old one). A stream handle that is
+ *              destroyed and created again keeps the workspace of the first:
+ *              destroy a stream only after its work has finished.
  *   {U}:       an f32 output marked {U} is a partial sum ("unreduced" in
  *              [TPSP]/[SB6] notation): the full result is the sum of the t
  *              ranks' outputs. The exchange that sums them (an all-reduce) is
