@@ -354,9 +354,19 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     ms_eager = time_fn(regroup, max(reps, 32), warm=4)[0]
     ms = time_graph(regroup, 32)
     moved = 2 * h * (width // t) * 2
+    # context: a plain device copy of the same bytes (contiguous), same graph timing
+    it[0] = 0
+
+    def plain_copy():
+        i = it[0]
+        it[0] += 1
+        dsts[i % 4].view(-1).copy_(srcs[i % 4].view(-1)[: h * (width // t)])
+
+    ms_copy = time_graph(plain_copy, 32)
     res["qkv_regroup"] = {"ms": round(ms, 5), "ms_eager": round(ms_eager, 5), "bytes": moved,
                           "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
-                          "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+                          "frac_hbm": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                          "plain_copy_ms": round(ms_copy, 5)}
     # the same at t = 16 > n_kv = 8: each KV head replicated on two ranks
     t16 = 16
     w16 = T.regroup_width(n_h, n_kv, d_h, t16)
@@ -403,7 +413,7 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
         T.tp_col_linear(X, W_r, "none", Y=Y)
         T.tp_row_linear_partial(O, W_O, P=P)
 
-    ms = time_fn(attn_fwd, reps)[0]
+    ms = time_fn(attn_fwd, reps, warm=8)[0]
     res["attn_proj_fwd_prefill"] = {"ms": round(ms, 4), "gflop": round(fl_fwd / 1e9, 2),
                                     "tflops": round(fl_fwd / (ms * 1e-3) / 1e12, 1)}
     dXq = torch.empty((Nq, h), dtype=f32, device=dev)
@@ -415,7 +425,7 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
         T.tp_col_linear_bwd(X, W_r, dQKV, dX_part=dXq, dW=dWq)
         T.tp_row_linear_bwd(O, W_O, dY, dZ=dO, dW=dWO)
 
-    ms = time_fn(attn_bwd, reps)[0]
+    ms = time_fn(attn_bwd, reps, warm=8)[0]
     res["attn_proj_bwd_prefill"] = {"ms": round(ms, 4), "gflop": round(2 * fl_fwd / 1e9, 2),
                                     "tflops": round(2 * fl_fwd / (ms * 1e-3) / 1e12, 1)}
     del dXq, dWq, dO, dWO, Y, P
@@ -436,9 +446,20 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     ms_eager = time_fn(decode, max(reps, 32), warm=4)[0]
     ms = time_graph(decode, 16)
     wbytes = 2 * h * (width // t) + 2 * (n_h * d_h // t) * h
+    # context: the vendor BLAS on the same two products (bf16 outputs), same graph timing
+    it[0] = 0
+
+    def decode_blas():
+        i = it[0] % 16
+        it[0] += 1
+        torch.matmul(Xd, Wrs[i], out=Yd)
+        torch.matmul(Od, WOs[i])
+
+    ms_blas = time_graph(decode_blas, 16)
     res["attn_proj_decode_n16"] = {"ms": round(ms, 4), "ms_eager": round(ms_eager, 4), "weight_bytes": wbytes,
                                    "gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
-                                   "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+                                   "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                                   "blas_ms": round(ms_blas, 4)}
     del Wrs, WOs, X, O, dQKV, dY, W_r, W_O
 
     # --- Llama-3-70B vocab-parallel LM head + fused cross-entropy, one shard of 8 ---
@@ -508,7 +529,11 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     shapes, bf16 in and out, plain product without the epilogues. Not part of
     the measured path."""
     shapes = {"gemm1_gate_up": (N, h, 2 * f), "gemm2_down": (N, f, h), "dx": (N, 2 * f, h),
-              "dw_gate_up": (h, N, 2 * f), "dw_down": (f, N, h)}
+              "dw_gate_up": (h, N, 2 * f), "dw_down": (f, N, h),
+              # the Llama-3-70B attention projections of one rank (t = 8), prefill:
+              # QKV and W_O forward, then dX, dW of QKV and dO, dW of W_O
+              "attn_qkv": (N, h, 1280), "attn_wo": (N, 1024, h), "attn_dx_qkv": (N, 1280, h),
+              "attn_dw_qkv": (h, N, 1280), "attn_do": (N, h, 1024), "attn_dw_o": (1024, N, h)}
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     res = {}
@@ -518,7 +543,17 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
         ms = time_fn(lambda: a @ b, reps)[0]
         res[name] = {"ms": round(ms, 4), "tflops": round(2 * M * K * Nn / (ms * 1e-3) / 1e12, 1)}
         del a, b
-    log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()))
+    log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()
+                                                       if not k.startswith("attn")))
+    fa = sum(2 * shapes[k][0] * shapes[k][1] * shapes[k][2] for k in ("attn_qkv", "attn_wo"))
+    fb = sum(2 * shapes[k][0] * shapes[k][1] * shapes[k][2]
+             for k in ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o"))
+    ta = sum(res[k]["ms"] for k in ("attn_qkv", "attn_wo"))
+    tb = sum(res[k]["ms"] for k in ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o"))
+    res["attn_fwd_total"] = {"ms": round(ta, 4), "tflops": round(fa / (ta * 1e-3) / 1e12, 1)}
+    res["attn_bwd_total"] = {"ms": round(tb, 4), "tflops": round(fb / (tb * 1e-3) / 1e12, 1)}
+    log(f"[bench] vendor BLAS attention projections: fwd {res['attn_fwd_total']['tflops']}, "
+        f"bwd {res['attn_bwd_total']['tflops']} TFLOP/s")
     return res
 
 
