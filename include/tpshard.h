@@ -32,8 +32,9 @@
  *              needed (after synchronising that stream) and keeps until the
  *              process ends: ksplit * N * n * 4 bytes for a split product
  *              (a few MB at decode sizes, up to ~70 MB for the Llama-3-70B
- *              attention shards). No call allocates anything else. Calls on
- *              one stream are ordered, so they cannot race on it. A call
+ *              attention shards); tp_vocab_embed_bwd keeps 4 bytes per table
+ *              row there. No call allocates anything else. Calls on one
+ *              stream are ordered, so they cannot race on it. A call
  *              reserves what it needs before it enqueues anything: a failed
  *              allocation returns TP_ERR_HIP, and growing it while the
  *              stream is being captured into a graph returns
@@ -311,6 +312,7 @@ tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_
  * Its backward: dE_i f32 [v_loc, h], row v = the sum of dY[n] over the tokens
  * n whose id is vocab_start + v, added in token order (deterministic); rows
  * no token uses are zero. dY f32 [N, h]. h <= 16384 (else UNSUPPORTED).
+ * Uses 4 bytes per table row of the stream's workspace (see Workspace).
  */
 tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_start,
                              int64_t N, int64_t v_loc, int64_t h, float* dE_i,

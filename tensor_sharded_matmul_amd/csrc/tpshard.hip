@@ -502,17 +502,39 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restric
 // rows added in that order. Masks and lists alternate between two LDS
 // buffers, so a chunk without a match costs one barrier. Every row's sum is
 // taken in token order: the result does not depend on scheduling.
+// Most rows of a shard receive no token (4096 tokens over 16032 rows of a
+// Llama-3 shard), and for those the scan is wasted: a first kernel stamps
+// every row some token uses with this call's number, and a row whose stamp
+// differs writes its zeros without scanning. The stamps live in the
+// stream's workspace, whose other users leave arbitrary bits there; a stale
+// or accidental match only costs a scan that finds nothing, so the result
+// never depends on the stamps' earlier contents.
 constexpr int kEmbedMaxH = 16384;
+
+__global__ void __launch_bounds__(256) embed_mark_kernel(const int32_t* __restrict__ ids, int64_t vocab_start,
+                                                         int64_t N, int v_loc, uint32_t* __restrict__ stamp,
+                                                         uint32_t cur) {
+    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t v = (int64_t)ids[n] - vocab_start;
+        if (v >= 0 && v < v_loc) stamp[v] = cur;  // every writer of a row writes the same value
+    }
+}
 
 __global__ void __launch_bounds__(256) embed_bwd_kernel(const int32_t* __restrict__ ids,
                                                         const float* __restrict__ dY, int64_t vocab_start,
-                                                        int N, int h, float* __restrict__ dE) {
+                                                        int N, int h, float* __restrict__ dE,
+                                                        const uint32_t* __restrict__ stamp, uint32_t cur) {
     constexpr int Q = kEmbedMaxH / 1024;  // column quads per thread
     constexpr int U = 16;                 // id chunks loaded at a time
     __shared__ int list[2][256];
     __shared__ uint64_t masks[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t target = vocab_start + blockIdx.x;
+    if (stamp[blockIdx.x] != cur) {  // no token uses this row (uniform)
+        float* row = dE + (int64_t)blockIdx.x * h;
+        for (int c = tid * 4; c < h; c += 1024) *reinterpret_cast<f32x4_t*>(row + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
     f32x4_t acc[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1046,8 +1068,20 @@ tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_
     if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
     TP_CHECK_TOK_PTR(dY, "dY");
     TP_CHECK_PTR(dE_i, "dE_i");
-    hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)v_loc), dim3(256), 0, static_cast<hipStream_t>(stream), ids,
-                       dY, vocab_start, (int)N, (int)h, dE_i);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* ws = nullptr;
+    TP_TRY(workspace(fn, s, (size_t)v_loc * sizeof(uint32_t), &ws));
+    uint32_t* stamp = reinterpret_cast<uint32_t*>(ws);
+    static std::atomic<uint32_t> g_stamp{0};
+    uint32_t cur = ++g_stamp;
+    if (cur == 0) cur = ++g_stamp;  // after 2^32 calls; any value works, see the kernels
+    if (N > 0) {
+        const unsigned mark_blocks = (unsigned)std::min<int64_t>((N + 255) / 256, 1024);
+        hipLaunchKernelGGL(embed_mark_kernel, dim3(mark_blocks), dim3(256), 0, s, ids, vocab_start, N, (int)v_loc,
+                           stamp, cur);
+    }
+    hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)v_loc), dim3(256), 0, s, ids, dY, vocab_start, (int)N,
+                       (int)h, dE_i, stamp, cur);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
