@@ -502,13 +502,14 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restric
 // rows added in that order. Masks and lists alternate between two LDS
 // buffers, so a chunk without a match costs one barrier. Every row's sum is
 // taken in token order: the result does not depend on scheduling.
-// Most rows of a shard receive no token (4096 tokens over 16032 rows of a
-// Llama-3 shard), and for those the scan is wasted: a first kernel stamps
-// every row some token uses with this call's number, and a row whose stamp
-// differs writes its zeros without scanning. The stamps live in the
-// stream's workspace, whose other users leave arbitrary bits there; a stale
-// or accidental match only costs a scan that finds nothing, so the result
-// never depends on the stamps' earlier contents.
+// Most rows of a shard receive no token (4096 tokens over Llama-3's 128256
+// ids put about 512 into a shard's 16128 rows), and for those the scan is
+// wasted: a first kernel stamps every row some token uses with this call's
+// number, and a row whose stamp differs writes its zeros without scanning.
+// The stamps live in the stream's workspace, whose other users leave
+// arbitrary bits there; a stale or accidental match only costs a scan that
+// finds nothing, so the result never depends on the stamps' earlier
+// contents.
 constexpr int kEmbedMaxH = 16384;
 
 __global__ void __launch_bounds__(256) embed_mark_kernel(const int32_t* __restrict__ ids, int64_t vocab_start,
