@@ -59,14 +59,16 @@ int device_cus();
 // LDS rings per operand layout: K-contiguous operands in stages of 64 k-rows
 // (a tile row is one whole 128-byte line), MN-contiguous ones in 32-row
 // stages. Depths are the fastest measured on MI355X for the Llama-3-70B
-// shard products (a deeper ring or the full 160 KB of LDS did not help).
+// shard products. NT fills the 160 KB of LDS with a third B stage (dX and
+// dZ products 2-3 % faster than with two); for NN and TN a deeper ring or
+// the full LDS did not help.
 template <bool A_T, bool B_KN>
 struct Rings;
 #ifndef TPS_NN_RING
 #define TPS_NN_RING 64, 2, 32, 4
 #endif
 #ifndef TPS_NT_RING
-#define TPS_NT_RING 64, 2, 64, 2
+#define TPS_NT_RING 64, 2, 64, 3
 #endif
 #ifndef TPS_TN_RING
 #define TPS_TN_RING 32, 4, 32, 3
@@ -78,7 +80,7 @@ struct RingOf {
 template <>
 struct Rings<false, true> : RingOf<TPS_NN_RING> {};   // NN: A K-contiguous, B MN-contiguous (128 KB)
 template <>
-struct Rings<false, false> : RingOf<TPS_NT_RING> {};  // NT: both K-contiguous (128 KB)
+struct Rings<false, false> : RingOf<TPS_NT_RING> {};  // NT: both K-contiguous (160 KB)
 template <>
 struct Rings<true, true> : RingOf<TPS_TN_RING> {};    // TN: both MN-contiguous (106 KB)
 
