@@ -69,9 +69,9 @@ def committed_traffic(product: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("product") != product or t.get("kernel_sources_sha") != kernel_sources_sha():
+    if t.get("kernel_sources_sha") != kernel_sources_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("products", {}).get(product, {}).get("hbm_bytes_per_launch")
 
 
 def log(*a):
