@@ -181,8 +181,11 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
 
-    def time_fn(fn, reps, warm=2):
-        """Average ms per call: one HIP event pair per call on the launch stream."""
+    def time_fn(fn, reps, warm=2, inner=4):
+        """ms per call: `reps` HIP event pairs on the launch stream, each around
+        `inner` back-to-back calls, so that the GPU queue stays full and the
+        binding's host time per call (about 10 us) is not counted for kernels
+        longer than that; mean, median and min over the pairs."""
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
@@ -190,10 +193,11 @@ def main() -> int:
                for _ in range(reps)]
         for a, b in evs:
             a.record(stream)
-            fn()
+            for _ in range(inner):
+                fn()
             b.record(stream)
         torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in evs]
+        ts = [a.elapsed_time(b) / inner for a, b in evs]
         return float(np.mean(ts)), float(np.median(ts)), float(np.min(ts))
 
     def time_graph(fn, calls, replays=8):
