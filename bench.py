@@ -99,7 +99,7 @@ def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the TP layer; --gpus {args.gpus} is not "
-              "supported (this build runs on a single GPU and has no collectives).", file=sys.stderr)
+              "supported (the library computes one GPU's share of the layer and has no collectives).", file=sys.stderr)
         return 2
     import numpy as np
     import torch
