@@ -92,6 +92,9 @@ def parse():
     ap.add_argument("--regroup-only", type=int, default=0, metavar="CALLS",
                     help="only run the fused-QKV regroup CALLS times (4 rotated sources, ranks 0..7; "
                          "for profiling), then exit")
+    ap.add_argument("--decode-only", type=int, default=0, metavar="CALLS",
+                    help="only run the decode-sized (16 tokens) QKV and W_O products of the Llama-3-70B "
+                         "attention shard CALLS times (16 rotated weight copies; for profiling), then exit")
     return ap.parse_args()
 
 
@@ -131,6 +134,23 @@ def main() -> int:
             T.tp_qkv_regroup(srcs[i % 4], q.n_h, q.n_kv, q.d_h, q.t, (i // 4) % q.t, W_r=dsts[i % 4])
         torch.cuda.synchronize()
         log(f"[bench] regrouped {args.regroup_only} times")
+        return 0
+    if args.decode_only:
+        q = synth.WORKLOADS["llama70b_qkv_t8"]
+        wq, wo = (q.n_h + 2 * q.n_kv) * q.d_h // q.t, q.n_h * q.d_h // q.t
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(q.seed)
+        rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+        Xd, Od = rnd(16, q.h), rnd(16, wo)
+        Wrs = [rnd(q.h, wq) for _ in range(16)]
+        WOs = [rnd(wo, q.h) for _ in range(16)]
+        Yd = torch.empty((16, wq), device=dev, dtype=torch.bfloat16)
+        Pd = torch.empty((16, q.h), device=dev, dtype=torch.float32)
+        for i in range(args.decode_only):
+            T.tp_col_linear(Xd, Wrs[i % 16], "none", Y=Yd)
+            T.tp_row_linear_partial(Od, WOs[i % 16], P=Pd)
+        torch.cuda.synchronize()
+        log(f"[bench] decode products run {args.decode_only} times")
         return 0
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
@@ -302,6 +322,42 @@ def main() -> int:
                             "overhead": round(ms_c / kt["gemm2_down_partial"]["ms"] - 1, 3)}
     if chunked:
         kt["gemm2_down_partial_chunked"] = chunked
+
+    # Epilogue fusion, for context: the same products with a plain bf16 store,
+    # then the activation (or its derivative) as a separate elementwise pass
+    # in eager torch (several kernels). A single ideal pass would move 84 MiB
+    # forward (read G, U; write Z) and 140 MiB backward (read dZ, G, U; write
+    # dG, dU); its rate is reported against those bytes.
+    if not args.no_rows:
+        Hp = torch.empty((N, 2 * f), dtype=bf, device=dev)
+        Zp = torch.empty((N, f), dtype=bf, device=dev)
+        dZp = torch.empty((N, f), dtype=bf, device=dev)
+        dHp = torch.empty((N, 2 * f), dtype=bf, device=dev)
+
+        def act_fwd():
+            torch.mul(torch.nn.functional.silu(Hp[:, :f]), Hp[:, f:], out=Zp)
+
+        def act_bwd():
+            g, u, dz = H[:, :f].float(), H[:, f:].float(), dZp.float()
+            sg = torch.sigmoid(g)
+            dHp[:, :f] = dz * u * sg * (1 + g * (1 - sg))
+            dHp[:, f:] = dz * g * sg
+
+        g1p = time_fn(lambda: T.tp_col_linear(X, W_in, "none", Y=Hp), args.reps)[0]
+        afp = time_fn(act_fwd, args.reps)[0]
+        dzp = time_fn(lambda: T.tp_row_linear_bwd(Z, W_out, dY, dZ=dZp, want_dw=False), args.reps)[0]
+        abp = time_fn(act_bwd, args.reps)[0]
+        mib = 1 << 20
+        kt["epilogue_fusion"] = {
+            "fwd": {"fused_ms": kt["gemm1_gate_up_swiglu"]["ms"], "plain_gemm_ms": round(g1p, 4),
+                    "separate_pass_ms": round(afp, 4), "pass_ideal_bytes": 84 * mib,
+                    "pass_gbs_vs_ideal_bytes": round(84 * mib / (afp * 1e-3) / 1e9, 1)},
+            "bwd": {"fused_ms": kt["bwd_dz_swiglu"]["ms"], "plain_gemm_ms": round(dzp, 4),
+                    "separate_pass_ms": round(abp, 4), "pass_ideal_bytes": 140 * mib,
+                    "pass_gbs_vs_ideal_bytes": round(140 * mib / (abp * 1e-3) / 1e9, 1)},
+        }
+        log(f"[bench] epilogue fusion: {kt['epilogue_fusion']}")
+        del Hp, Zp, dZp, dHp
 
     rows = {"mlp_kernels": kt,
             "fwd_ms": round(time_fn(fwd, args.reps)[0], 4), "bwd_ms": round(bwd_mean, 4)}

@@ -786,10 +786,17 @@ gemm_kernel(const GemmArgs args) {
     } else {
         db.init(wave, lane, 0, args.ldb);
     }
+    // An MN-contiguous operand of a split-K product is range-checked up to
+    // the end of this split's K rows: the ring's loads past the chunk (issued
+    // to keep the waits constant) then read zeros instead of fetching the
+    // next split's rows from memory.
+    const uint64_t k_end = (uint64_t)(k0 + Kloc);
+    const uint64_t a_ext = (A_T && args.ksplit > 1) ? min(args.a_bytes, k_end * (uint64_t)args.lda * 2u) : args.a_bytes;
+    const uint64_t b_ext = (B_KN && args.ksplit > 1) ? min(args.b_bytes, k_end * (uint64_t)args.ldb * 2u) : args.b_bytes;
     StageCursor<A_T && WIDE> ca;
     StageCursor<B_KN && WIDE> cb;
-    ca.init(args.A, args.a_bytes, a_org, A_T ? (uint64_t)BKA * (uint64_t)args.lda * 2u : (uint64_t)BKA * 2u);
-    cb.init(args.B, args.b_bytes, b_org, B_KN ? (uint64_t)BKB * (uint64_t)args.ldb * 2u : (uint64_t)BKB * 2u);
+    ca.init(args.A, a_ext, a_org, A_T ? (uint64_t)BKA * (uint64_t)args.lda * 2u : (uint64_t)BKA * 2u);
+    cb.init(args.B, b_ext, b_org, B_KN ? (uint64_t)BKB * (uint64_t)args.ldb * 2u : (uint64_t)BKB * 2u);
     const uint32_t ldsA = lds_addr(smem), ldsB = ldsA + SA * A_STAGE;
     constexpr int LA = ADma::kPerWave, LB = BDma::kPerWave;  // loads per stage per wave
     constexpr RingModel ring{PA, SA, LA, PB, SB, LB};
