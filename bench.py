@@ -14,8 +14,8 @@ regroup (GB/s, buffers rotated past the 256 MB Infinity Cache), the attention
 projections (QKV + W_O) forward and backward at N = 4096 and decode at N = 16,
 the GPT-style GeLU MLP shard (N = 8192, h = 4096, F = 16384, t = 4), and, as
 context, the ROCm BLAS library (torch.matmul) on the step's GEMM shapes. The
-fp64 oracle is timed on a bounded token sample of the same MLP workload on the
-host cores (cpu_baseline).
+fp64 oracle is timed on the same MLP workload (and, as legs, the GeLU shard
+and the attention projections) on the host cores (cpu_baseline).
 
 roofline: the step's dominant kernel (largest single launch), its FLOPs per
 launch over its average launch time (HIP events over back-to-back launches),
@@ -42,6 +42,7 @@ KERNEL_DESC = {
     "gemm1_gate_up_swiglu": "gemm_kernel NN, 256x224 tile (112 gate + 112 up columns in separate waves, "
                             "joined through LDS), SwiGLU epilogue",
     "gemm2_down_partial": "gemm_kernel NN, 256x256 tile, fp32 store",
+    "bwd_dz_swiglu": "gemm_kernel NT, 256x224 tile, 8 waves, SwiGLU backward epilogue reading H",
     "bwd_dx_partial": "gemm_kernel NT, 256x256 tile, fp32 store",
     "bwd_dw_gate_up": "gemm_kernel TN, 256x224 tile, 8 waves, fp32 store",
     "bwd_dw_down": "gemm_kernel TN, 224x256 tile, 8 waves, fp32 store",
@@ -85,8 +86,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=10, help="repetitions per single-kernel timing")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
-                    help="token sample for the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the workload the oracle CPU baseline runs (0 = skip)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (scale for HBM byte counters), then exit")
@@ -224,8 +225,7 @@ def main() -> int:
     def time_graph(fn, calls, replays=8):
         """Average ms per call of `fn` replayed from a HIP graph: `calls` calls
         are captured once on a side stream (after two eager warm-up rounds on
-        it, which also create the library's per-stream split-K workspace) and
-        the graph is replayed `replays` times between two events. For
+        it) and the graph is replayed `replays` times between two events. For
         launch-bound calls (decode, regroup) this is the GPU time without the
         Python binding's per-call host cost."""
         side = torch.cuda.Stream()
@@ -273,6 +273,9 @@ def main() -> int:
     kern = {
         "gemm1_gate_up_swiglu": lambda: T.tp_col_linear(X, W_in, "swiglu", Y=Z, H_save=H),
         "gemm2_down_partial": lambda: T.tp_row_linear_partial(Z, W_out, P=P),
+        # the backward call with no gradient requested: dZ = dY W_down^T with
+        # the SwiGLU backward epilogue (reads H, writes dH) alone
+        "bwd_dz_swiglu": lambda: T.tp_mlp_shard_bwd(X, W_in, W_out, H, Z, dY, "swiglu", dH=dH, want=()),
         "bwd_dx_partial": lambda: T.tp_col_linear_bwd(X, W_in, dH, dX_part=dX, want_dw=False),
         "bwd_dw_gate_up": lambda: T.tp_col_linear_bwd(X, W_in, dH, dW=dWi, want_dx=False),
         "bwd_dw_down": lambda: T.tp_row_linear_bwd(Z, W_out, dY, dW=dWo, want_dz=False),
@@ -284,9 +287,6 @@ def main() -> int:
                     "tflops": round(fl[name] / (mean * 1e-3) / 1e12, 1)}
         log(f"[bench] {name:24s} {mean:.4f} ms  {kt[name]['tflops']} TFLOP/s")
     bwd_mean = time_fn(bwd, args.reps)[0]
-    dz_ms = bwd_mean - sum(kt[k]["ms"] for k in ("bwd_dx_partial", "bwd_dw_gate_up", "bwd_dw_down"))
-    kt["bwd_dz_swiglu"] = {"ms": round(dz_ms, 4), "derived": "bwd total minus the other three",
-                           "tflops": round(fl["bwd_dz_swiglu"] / (dz_ms * 1e-3) / 1e12, 1)}
 
     # dominant kernel: the single launch with the largest share of the step,
     # timed over `reps` back-to-back launches on the launch stream
@@ -619,7 +619,11 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
 
 
 def cpu_baseline(d, dY_bits, n_tok, synth, np):
-    """The fp64 oracle as it stands, on the first n_tok tokens of the same MLP workload."""
+    """The fp64 oracle as it stands, timed on the host cores: the measured
+    workload's forward and backward (the backward from the forward's saved
+    tensors, as the GPU step does; the first n_tok tokens, 4096 = all), then
+    as legs the GPT GeLU shard forward and the Llama-3-70B attention
+    projections forward + backward at prefill size."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -634,16 +638,44 @@ def cpu_baseline(d, dY_bits, n_tok, synth, np):
     h, n_w = W_in.shape
     f = W_out.shape[0]
     t0 = time.perf_counter()
-    O.mlp_shard_fwd(X, W_in, W_out, "swiglu")
-    O.mlp_shard_bwd(X, W_in, W_out, dY, "swiglu")
+    Z, H, _ = O.mlp_shard_fwd(X, W_in, W_out, "swiglu")
+    O.mlp_shard_bwd_saved(X, W_in, W_out, H, Z, dY, "swiglu")
     dt = time.perf_counter() - t0
+    # GEMM1 + GEMM2 forward; dZ, dX, dW_in, dW_out backward: 3x the forward
     flops = 3 * (2 * n_tok * n_w * h + 2 * n_tok * h * f)
+    del X, W_in, W_out, dY, Z, H
     log(f"[bench] oracle fp64 on {n_tok} tokens: {dt:.2f}s, {flops / dt / 1e9:.1f} GFLOP/s, "
         f"{threads} threads")
+    legs = {}
+    g = synth.WORKLOADS["gpt_gelu_t4"]
+    dg = synth.mlp_inputs(g.seed, g.N, g.h, g.F, g.t, "gelu")
+    og = {k: synth.bf16_to_f64(v) for k, v in dg.items()}
+    t0 = time.perf_counter()
+    O.mlp_shard_fwd(og["X"], og["W_in"], og["W_out"], "gelu")
+    dtg = time.perf_counter() - t0
+    flg = 2 * 2 * g.N * g.h * g.f
+    legs["gpt_gelu_mlp_fwd_t4"] = {"s": round(dtg, 3), "gflop": round(flg / 1e9, 2),
+                                   "tflops": round(flg / dtg / 1e12, 4)}
+    del dg, og
+    q = synth.WORKLOADS["llama70b_qkv_t8"]
+    dq = synth.qkv_inputs(q.seed, q.N, q.h, q.n_h, q.n_kv, q.d_h, q.t)
+    Wr = synth.bf16_to_f64(O.qkv_regroup(dq["W_qkv"], q.n_h, q.n_kv, q.d_h, q.t, 0))
+    oq = {k: synth.bf16_to_f64(dq[k]) for k in ("X", "O", "W_O", "dQKV", "dY")}
+    t0 = time.perf_counter()
+    O.col_linear(oq["X"], Wr)
+    O.row_linear_partial(oq["O"], oq["W_O"])
+    O.col_linear_bwd(oq["X"], Wr, oq["dQKV"])
+    O.row_linear_bwd(oq["O"], oq["W_O"], oq["dY"])
+    dtq = time.perf_counter() - t0
+    flq = 3 * (2 * q.N * q.h * Wr.shape[1] + 2 * q.N * oq["W_O"].shape[0] * q.h)
+    legs["attn_proj_fwd_bwd_prefill"] = {"s": round(dtq, 3), "gflop": round(flq / 1e9, 2),
+                                         "tflops": round(flq / dtq / 1e12, 4)}
+    log(f"[bench] oracle legs: {legs}")
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"MLP shard fwd+bwd on the first {n_tok} of 4096 tokens (fp64 numpy/OpenBLAS); "
-                      f"{dt:.2f} s for {flops / 1e9:.1f} GFLOP"}
+            "sample": f"the measured step (MLP shard fwd + bwd from saved tensors) on {n_tok} of 4096 tokens, "
+                      f"fp64 numpy/OpenBLAS: {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
+            "legs": legs}
 
 
 if __name__ == "__main__":

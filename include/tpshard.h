@@ -25,20 +25,22 @@
  *              pointer to them after the call returns.
  *   Workspace: a product with too few output tiles for the CUs (N <= 64
  *              tokens, or a narrow shard such as the attention projections')
- *              splits K over workgroups and sums the f32 partials in a
- *              second kernel; tp_vocab_ce_fwd keeps per-tile records. Their
- *              scratch is one device buffer per (device, stream) that the
- *              library allocates on first use, grows when a larger one is
- *              needed (after synchronising that stream) and keeps until the
- *              process ends: ksplit * N * n * 4 bytes for a split product
- *              (a few MB at decode sizes, up to ~70 MB for the Llama-3-70B
- *              attention shards); tp_vocab_embed_bwd keeps 4 bytes per table
- *              row there. No call allocates anything else. Calls on one
- *              stream are ordered, so they cannot race on it. A call
- *              reserves what it needs before it enqueues anything: a failed
- *              allocation returns TP_ERR_HIP, and growing it while the
- *              stream is being captured into a graph returns
- *              TP_ERR_INVALID_ARG (run the call once on that stream first).
+ *              splits K over workgroups and sums their f32 partials in a
+ *              second kernel; tp_vocab_ce_fwd keeps per-tile records and
+ *              tp_vocab_embed_bwd per-row stamps. That scratch is device
+ *              memory the caller provides: every call that may need it takes
+ *              (void* workspace, size_t workspace_bytes), and the host-only
+ *              query of the same name plus "_workspace_size", given the same
+ *              sizes, returns how many bytes the call needs on the current
+ *              device (0: none, workspace may then be NULL). A call whose
+ *              workspace is NULL or smaller than that returns
+ *              TP_ERR_INVALID_ARG before enqueuing anything. The workspace
+ *              must be 16-byte aligned; its contents on entry do not matter
+ *              and are undefined afterwards. It is in use until the call's
+ *              work on `stream` has finished, so calls that may run at the
+ *              same time (on different streams) need different workspaces.
+ *              The library allocates no memory, keeps no pointer and never
+ *              synchronises: every call can be captured into a HIP graph.
  *   Sizes:     N (tokens) is any value from 0 to 2^30 (N = 0 is a no-op).
  *              Model widths (k, n, h, f, k_loc; the LM head's v_loc) must be positive
  *              multiples of 64 and at most 2^20 (larger: UNSUPPORTED). No
@@ -50,12 +52,9 @@
  *   Errors:    arguments are validated before any launch; on failure nothing
  *              is enqueued, a status != TP_OK is returned and a message is
  *              kept in thread-local storage (tp_last_error). Calls are
- *              re-entrant across threads as long as each stream is used by
- *              one host thread at a time (a stream's workspace may be
- *              replaced by a call on it while another thread still
- *              enqueues work that uses the old one). A stream handle that is
- *              destroyed and created again keeps the workspace of the first:
- *              destroy a stream only after its work has finished.
+ *              re-entrant across threads (the library holds no state besides
+ *              each thread's last error message and a counter of
+ *              tp_vocab_embed_bwd calls).
  *   {U}:       an f32 output marked {U} is a partial sum ("unreduced" in
  *              [TPSP]/[SB6] notation): the full result is the sum of the t
  *              ranks' outputs. The exchange that sums them (an all-reduce) is
@@ -66,6 +65,7 @@
 #ifndef TPSHARD_H
 #define TPSHARD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -86,7 +86,7 @@ typedef enum {
     TP_ACT_SWIGLU = 2  /* SiLU(gate) * up over [gate | up] weight halves      */
 } tp_act;
 
-/* Library version, (major << 16) | minor. */
+/* Library version, (major << 16) | minor (0.2: caller-owned workspaces). */
 int tp_version(void);
 
 /* Message of the last failed call on this thread ("" if none). The pointer
@@ -110,9 +110,12 @@ const char* tp_last_error(void);
  * Errors: INVALID_ARG (pointers, sizes, act), UNSUPPORTED (width not a
  * multiple of 64), HIP.
  */
+tp_status tp_col_linear_workspace_size(int64_t N, int64_t k, int64_t n_out,
+                                       int act, size_t* bytes);
 tp_status tp_col_linear(const void* X, const void* W, void* Y,
                         int64_t N, int64_t k, int64_t n_out, int act,
-                        void* H_save, void* stream);
+                        void* H_save, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Row-parallel linear, partial sum ([TPSP] "矩阵乘法的两种切法", second
@@ -123,9 +126,12 @@ tp_status tp_col_linear(const void* X, const void* W, void* Y,
  *   Z  bf16 [N, k_loc]   W  bf16 [k_loc, n]
  *   P  f32  [N, n] {U}   P = Z W, or P += Z W when accumulate != 0.
  */
+tp_status tp_row_linear_partial_workspace_size(int64_t N, int64_t k_loc,
+                                               int64_t n, size_t* bytes);
 tp_status tp_row_linear_partial(const void* Z, const void* W, float* P,
                                 int64_t N, int64_t k_loc, int64_t n,
-                                int accumulate, void* stream);
+                                int accumulate, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * The row-parallel partial computed in row chunks, for overlapping its
@@ -137,10 +143,14 @@ tp_status tp_row_linear_partial(const void* Z, const void* W, float* P,
  * is recorded on `stream`, so another stream can wait for exactly that
  * chunk. events may be NULL (no events). 1 <= nchunks <= 64.
  */
+tp_status tp_row_linear_partial_chunked_workspace_size(int64_t N, int64_t k_loc,
+                                                       int64_t n, int32_t nchunks,
+                                                       size_t* bytes);
 tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P,
                                         int64_t N, int64_t k_loc, int64_t n,
                                         int accumulate, int32_t nchunks,
-                                        void* const* events, void* stream);
+                                        void* const* events, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * One rank's MLP share, forward ([TPSP] "MLP：先列后行，只通信一次"): first
@@ -155,10 +165,12 @@ tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P,
  *   P      f32  [N, h] {U}   Z W_out (accumulate != 0: added into P)
  * act must be GELU or SWIGLU. f = F/t is the per-rank MLP width.
  */
+tp_status tp_mlp_shard_fwd_workspace_size(int64_t N, int64_t h, int64_t f,
+                                          int act, size_t* bytes);
 tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out,
                            int64_t N, int64_t h, int64_t f, int act,
                            void* Z, void* H_save, float* P, int accumulate,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One rank's MLP share, backward ([TPSP] "矩阵乘法的两种切法", backward
@@ -173,15 +185,22 @@ tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out,
  * Inputs: X bf16 [N,h], W_in bf16 [h,n_w], W_out bf16 [f,h], H_save bf16
  * [N,n_w] (the forward's pre-activation, required), Z bf16 [N,f] (the forward's
  * activation output, required), dY bf16 [N,h].
- * Outputs: dH bf16 [N,n_w] (also the caller-owned workspace of the two
- * GEMMs that follow), dX_part f32 [N,h] {U} (accumulate != 0 adds into it),
- * dW_in f32 [h,n_w], dW_out f32 [f,h]. dZ itself is never stored.
+ * Outputs: dH bf16 [N,n_w] (always written; the operand of the two
+ * products that follow), dX_part f32 [N,h] {U} (accumulate != 0 adds into
+ * it), dW_in f32 [h,n_w], dW_out f32 [f,h]. dZ itself is never stored.
+ * dX_part, dW_in and dW_out may each be NULL: that product is skipped (with
+ * all three NULL the call runs only dZ and the activation backward). X is
+ * read only for dW_in, W_in only for dX_part, Z only for dW_out.
+ * The workspace query counts all three products.
  */
+tp_status tp_mlp_shard_bwd_workspace_size(int64_t N, int64_t h, int64_t f,
+                                          int act, size_t* bytes);
 tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out,
                            const void* H_save, const void* Z, const void* dY,
                            int64_t N, int64_t h, int64_t f, int act,
                            void* dH, float* dX_part, float* dW_in, float* dW_out,
-                           int accumulate, void* stream);
+                           int accumulate, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * Column-parallel linear, backward ([TPSP] "矩阵乘法的两种切法": dX is a partial
@@ -190,10 +209,12 @@ tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out,
  *   dX_part f32 [N,k] {U} = dY W^T (NULL: skipped; accumulate != 0 adds)
  *   dW      f32 [k,n]     = X^T dY (NULL: skipped)
  */
+tp_status tp_col_linear_bwd_workspace_size(int64_t N, int64_t k, int64_t n,
+                                           size_t* bytes);
 tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY,
                             float* dX_part, float* dW,
                             int64_t N, int64_t k, int64_t n, int accumulate,
-                            void* stream);
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Row-parallel linear, backward ([TPSP] "矩阵乘法的两种切法": both gradients are
@@ -202,9 +223,12 @@ tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY,
  *   dZ bf16 [N,k_loc] = dY W^T (NULL: skipped)
  *   dW f32  [k_loc,n] = Z^T dY (NULL: skipped)
  */
+tp_status tp_row_linear_bwd_workspace_size(int64_t N, int64_t k_loc, int64_t n,
+                                           size_t* bytes);
 tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY,
                             void* dZ, float* dW,
-                            int64_t N, int64_t k_loc, int64_t n, void* stream);
+                            int64_t N, int64_t k_loc, int64_t n,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Per-rank regroup of the fused QKV weight ([TPSP] attention section, fused
@@ -256,12 +280,15 @@ tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h,
  *   m_i, s_i, zy_i f32 [N]: per token the local max of z, sum of
  *   exp(z - m_i) over the rank's range, and z of the target when the target
  *   is in the range (0 otherwise).
- * Uses the library's per-stream workspace for per-tile records
- * (N * 2 * ceil(v_loc / 224) * 12 bytes).
+ * Its workspace holds per-tile records: N * 2 * ceil(v_loc / 224) * 12
+ * bytes.
  */
+tp_status tp_vocab_ce_fwd_workspace_size(int64_t N, int64_t h, int64_t v_loc,
+                                         size_t* bytes);
 tp_status tp_vocab_ce_fwd(const void* X, const void* W_i, const int32_t* targets,
                           int64_t vocab_start, int64_t N, int64_t h, int64_t v_loc,
-                          float* m_i, float* s_i, float* zy_i, void* stream);
+                          float* m_i, float* s_i, float* zy_i, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * The exchange of the fused cross-entropy, on one device (the page's three
@@ -285,11 +312,13 @@ tp_status tp_vocab_ce_combine(const float* m_parts, const float* s_parts,
  *   dW_i f32 [h,v_loc] = X^T dZ.
  *   m, S, dloss f32 [N] (dloss: the upstream gradient of each token's loss).
  */
+tp_status tp_vocab_ce_bwd_workspace_size(int64_t N, int64_t h, int64_t v_loc,
+                                         size_t* bytes);
 tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets,
                           int64_t vocab_start, const float* m, const float* S,
                           const float* dloss, int64_t N, int64_t h, int64_t v_loc,
                           void* dZ, float* dX_part, float* dW_i, int accumulate,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Vocab-parallel input embedding, one rank's share ([TPSP] "输入 embedding"):
@@ -312,11 +341,14 @@ tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_
  * Its backward: dE_i f32 [v_loc, h], row v = the sum of dY[n] over the tokens
  * n whose id is vocab_start + v, added in token order (deterministic); rows
  * no token uses are zero. dY f32 [N, h]. h <= 16384 (else UNSUPPORTED).
- * Uses 4 bytes per table row of the stream's workspace (see Workspace).
+ * Its workspace holds a 4-byte stamp per table row (v_loc * 4 bytes); any
+ * earlier contents are fine.
  */
+tp_status tp_vocab_embed_bwd_workspace_size(int64_t N, int64_t v_loc, int64_t h,
+                                            size_t* bytes);
 tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_start,
                              int64_t N, int64_t v_loc, int64_t h, float* dE_i,
-                             void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Shard arithmetic of a tensor over a device mesh ([SB6] §6.1): host only,

@@ -14,7 +14,7 @@ from scipy.special import erf
 __all__ = [
     "matmul_loops", "col_linear", "row_linear_partial", "gelu", "gelu_grad",
     "sigmoid", "silu", "silu_grad", "swiglu", "col_linear_act", "mlp_shard_fwd",
-    "mlp_shard_bwd", "mlp_shard_fwd_rows", "mlp_shard_bwd_rows",
+    "mlp_shard_bwd", "mlp_shard_bwd_saved", "mlp_shard_fwd_rows", "mlp_shard_bwd_rows",
     "mlp_shard_bwd_cols", "col_linear_bwd", "row_linear_bwd",
     "qkv_regroup_index", "qkv_regroup", "naive_split_index", "shard_shape",
     "kv_heads_of_rank", "kv_replica_ranks", "kv_grad_accumulate", "kv_replica_grad_sum",
@@ -184,22 +184,31 @@ def _act_bwd(H, dZ, act):
     raise ValueError(act)
 
 
-def mlp_shard_bwd(X, W_in, W_out, dY, act):
-    """Backward of one rank's MLP share, from the upstream gradient dY[N,h].
+def mlp_shard_bwd_saved(X, W_in, W_out, H, Z, dY, act):
+    """Backward of one rank's MLP share from the forward's saved tensors.
 
-    Row-parallel backward of the second matrix (local): dZ = dY W_out^T,
-    dW_out = Z^T dY; activation backward to dH; column-parallel backward of
-    the first matrix: dX partial = dH W_in^T ({U}, completed by f's
-    all-reduce), dW_in = X^T dH (local). The forward tensors are recomputed
-    here in fp64 from X and the weights.
-    Returns dict(dZ, dH, dX_part, dW_in, dW_out, Z, H).
+    H = X W_in (the pre-activation) and Z = act(H) are the ones the forward
+    keeps ([TPSP] "显存账": gate, up and the activation output are stored for
+    the backward). Row-parallel backward of the second matrix (local):
+    dZ = dY W_out^T, dW_out = Z^T dY; activation backward to dH;
+    column-parallel backward of the first matrix: dX partial = dH W_in^T
+    ({U}, completed by f's all-reduce), dW_in = X^T dH (local).
+    Returns dict(dZ, dH, dX_part, dW_in, dW_out).
     """
-    Z, H, _ = mlp_shard_fwd(X, W_in, W_out, act)
     dZ, dW_out = row_linear_bwd(Z, W_out, dY)
-    dH = _act_bwd(H, dZ, act)
+    dH = _act_bwd(np.asarray(H, np.float64), dZ, act)
     dX_part, dW_in = col_linear_bwd(X, W_in, dH)
-    return {"dZ": dZ, "dH": dH, "dX_part": dX_part, "dW_in": dW_in, "dW_out": dW_out,
-            "Z": Z, "H": H}
+    return {"dZ": dZ, "dH": dH, "dX_part": dX_part, "dW_in": dW_in, "dW_out": dW_out}
+
+
+def mlp_shard_bwd(X, W_in, W_out, dY, act):
+    """Backward of one rank's MLP share, from the upstream gradient dY[N,h]:
+    the forward tensors computed here in fp64 from X and the weights, then
+    mlp_shard_bwd_saved. Returns dict(dZ, dH, dX_part, dW_in, dW_out, Z, H)."""
+    Z, H = col_linear_act(X, W_in, act)
+    g = mlp_shard_bwd_saved(X, W_in, W_out, H, Z, dY, act)
+    g["Z"], g["H"] = Z, H
+    return g
 
 
 def mlp_shard_fwd_rows(X, W_in, W_out, act, rows):

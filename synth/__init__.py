@@ -26,6 +26,8 @@ from __future__ import annotations
 import hashlib
 from dataclasses import dataclass, field
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -173,10 +175,12 @@ def vocab_ce_inputs(seed: int, N: int, h: int, v_loc: int, V: int):
     return {"X": X, "W_i": W_i, "targets": targets, "dloss": dloss}
 
 
-def int_inputs(seed: int, shape, lo: int = -2, hi: int = 2) -> np.ndarray:
-    """Small integers in [lo, hi] as bf16 bit patterns (exact in bfloat16)."""
+def int_inputs(seed: int, shape, lo: int = -2, hi: int = 2, scale: float = 1.0) -> np.ndarray:
+    """Small integers in [lo, hi], times `scale` (a power of two), as bf16 bit
+    patterns (exact in bfloat16)."""
+    assert scale > 0 and math.frexp(scale)[0] == 0.5, "scale must be a power of two"
     rng = np.random.default_rng(seed)
-    x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    x = rng.integers(lo, hi + 1, size=shape).astype(np.float32) * np.float32(scale)
     return bf16_round(x)
 
 

@@ -21,7 +21,9 @@ __all__ = [
     "lib_path", "load", "tp_version", "tp_last_error", "tp_col_linear",
     "tp_row_linear_partial", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
     "tp_col_linear_bwd", "tp_row_linear_bwd", "tp_qkv_regroup", "tp_shard_shape",
-    "ACT", "TPError",
+    "tp_row_linear_partial_chunked", "tp_kv_grad_accumulate", "tp_vocab_ce_fwd",
+    "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_embed_fwd", "tp_vocab_embed_bwd",
+    "workspace_size", "regroup_width", "ACT", "TPError",
 ]
 
 ACT = {"none": 0, "gelu": 1, "swiglu": 2}
@@ -50,30 +52,38 @@ def load():
         raise RuntimeError(f"{path} is not built; run `python -m tensor_sharded_matmul_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sz, psz = ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)
+    i = ctypes.c_int
     sigs = {
-        "tp_version": ([], ctypes.c_int),
+        "tp_version": ([], i),
         "tp_last_error": ([], ctypes.c_char_p),
-        "tp_col_linear": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp], ctypes.c_int),
-        "tp_row_linear_partial": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp], ctypes.c_int),
-        "tp_mlp_shard_fwd": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp, ctypes.c_int, vp],
-                             ctypes.c_int),
-        "tp_mlp_shard_bwd": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
-                              ctypes.c_int, vp], ctypes.c_int),
-        "tp_col_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp], ctypes.c_int),
-        "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
-        "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], ctypes.c_int),
-        "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], ctypes.c_int),
-        "tp_vocab_embed_fwd": ([vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp], ctypes.c_int),
-        "tp_vocab_embed_bwd": ([vp, vp, i64, i64, i64, i64, vp, vp], ctypes.c_int),
-        "tp_row_linear_partial_chunked": ([vp, vp, vp, i64, i64, i64, ctypes.c_int, i32,
-                                           ctypes.POINTER(vp), vp], ctypes.c_int),
-        "tp_vocab_ce_fwd": ([vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp], ctypes.c_int),
-        "tp_vocab_ce_combine": ([vp, vp, vp, i32, i64, vp, vp, vp, vp], ctypes.c_int),
-        "tp_vocab_ce_bwd": ([vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp, vp, ctypes.c_int, vp],
-                            ctypes.c_int),
+        "tp_col_linear_workspace_size": ([i64, i64, i64, i, psz], i),
+        "tp_col_linear": ([vp, vp, vp, i64, i64, i64, i, vp, vp, sz, vp], i),
+        "tp_row_linear_partial_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_row_linear_partial": ([vp, vp, vp, i64, i64, i64, i, vp, sz, vp], i),
+        "tp_row_linear_partial_chunked_workspace_size": ([i64, i64, i64, i32, psz], i),
+        "tp_row_linear_partial_chunked": ([vp, vp, vp, i64, i64, i64, i, i32, ctypes.POINTER(vp), vp, sz, vp], i),
+        "tp_mlp_shard_fwd_workspace_size": ([i64, i64, i64, i, psz], i),
+        "tp_mlp_shard_fwd": ([vp, vp, vp, i64, i64, i64, i, vp, vp, vp, i, vp, sz, vp], i),
+        "tp_mlp_shard_bwd_workspace_size": ([i64, i64, i64, i, psz], i),
+        "tp_mlp_shard_bwd": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, vp, vp, vp, i, vp, sz, vp], i),
+        "tp_col_linear_bwd_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_col_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp], i),
+        "tp_row_linear_bwd_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], i),
+        "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], i),
+        "tp_kv_grad_accumulate": ([vp, vp, i64, i32, i32, i32, i32, vp], i),
+        "tp_vocab_embed_fwd": ([vp, vp, i64, i64, i64, i64, vp, i, vp], i),
+        "tp_vocab_embed_bwd_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_vocab_embed_bwd": ([vp, vp, i64, i64, i64, i64, vp, vp, sz, vp], i),
+        "tp_vocab_ce_fwd_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_vocab_ce_fwd": ([vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp], i),
+        "tp_vocab_ce_combine": ([vp, vp, vp, i32, i64, vp, vp, vp, vp], i),
+        "tp_vocab_ce_bwd_workspace_size": ([i64, i64, i64, psz], i),
+        "tp_vocab_ce_bwd": ([vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp, vp, i, vp, sz, vp], i),
         "tp_shard_shape": ([i32, ctypes.POINTER(i64), i32, i32, ctypes.POINTER(i64),
                             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64),
-                            ctypes.POINTER(i64), ctypes.POINTER(i64)], ctypes.c_int),
+                            ctypes.POINTER(i64), ctypes.POINTER(i64)], i),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -128,6 +138,33 @@ def _out(t, name, dtype, shape, like):
 _bf16, _f32 = torch.bfloat16, torch.float32
 
 
+def workspace_size(entry: str, *sizes) -> int:
+    """Bytes of workspace the C call `entry` needs for these sizes on the
+    current device (its host-only `<entry>_workspace_size` query)."""
+    n = ctypes.c_size_t(0)
+    _check(getattr(load(), entry + "_workspace_size")(*sizes, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(entry, sizes, like, stream, workspace=None):
+    """(pointer, bytes, tensor) of the workspace for one call: the caller's
+    `workspace` tensor if given (any dtype, contiguous, on the GPU), else a
+    torch allocation of exactly the queried size (none if it is 0). A tensor
+    allocated here is kept by the caching allocator for the stream the call
+    runs on until that stream's work is done."""
+    if workspace is not None:
+        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), workspace
+    n = workspace_size(entry, *sizes)
+    if n == 0:
+        return ctypes.c_void_p(0), 0, None
+    ws = torch.empty(n, dtype=torch.uint8, device=like.device)
+    if stream is not None and stream != torch.cuda.current_stream(like.device):
+        ws.record_stream(stream)
+    return ctypes.c_void_p(ws.data_ptr()), n, ws
+
+
 def tp_version() -> int:
     return load().tp_version()
 
@@ -136,7 +173,7 @@ def tp_last_error() -> str:
     return load().tp_last_error().decode(errors="replace")
 
 
-def tp_col_linear(X, W, act="none", Y=None, H_save=None, want_h=False, stream=None):
+def tp_col_linear(X, W, act="none", Y=None, H_save=None, want_h=False, workspace=None, stream=None):
     """Y = act(X W) (SwiGLU: W = [gate | up]); returns (Y, H_save or None)."""
     lib = load()
     a = ACT[act]
@@ -150,12 +187,13 @@ def tp_col_linear(X, W, act="none", Y=None, H_save=None, want_h=False, stream=No
         H_save = torch.empty((N, n_w), dtype=_bf16, device=X.device)
     if H_save is not None:
         _dev(H_save, "H_save", _bf16, (N, n_w))
-    _check(lib.tp_col_linear(_ptr(X), _ptr(W), _ptr(Y), N, k, n_out, a, _ptr(H_save),
+    wp, wn, _keep = _workspace("tp_col_linear", (N, k, n_out, a), X, stream, workspace)
+    _check(lib.tp_col_linear(_ptr(X), _ptr(W), _ptr(Y), N, k, n_out, a, _ptr(H_save), wp, wn,
                              _stream(stream)))
     return Y, H_save
 
 
-def tp_row_linear_partial(Z, W, P=None, accumulate=False, stream=None):
+def tp_row_linear_partial(Z, W, P=None, accumulate=False, workspace=None, stream=None):
     """P = Z W (or P += Z W), f32 partial sum; returns P."""
     lib = load()
     N, k_loc = Z.shape
@@ -163,12 +201,14 @@ def tp_row_linear_partial(Z, W, P=None, accumulate=False, stream=None):
     _dev(Z, "Z", _bf16, (N, k_loc))
     _dev(W, "W", _bf16, (k_loc, n))
     P = _out(P, "P", _f32, (N, n), Z)
-    _check(lib.tp_row_linear_partial(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
+    wp, wn, _keep = _workspace("tp_row_linear_partial", (N, k_loc, n), Z, stream, workspace)
+    _check(lib.tp_row_linear_partial(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)), wp, wn,
                                      _stream(stream)))
     return P
 
 
-def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, events=None, stream=None):
+def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, events=None, workspace=None,
+                                  stream=None):
     """P = Z W (or P += Z W) in nchunks token-row chunks; events: None or nchunks
     torch.cuda.Event objects, each recorded after its chunk. Returns P."""
     lib = load()
@@ -185,13 +225,14 @@ def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, event
             if not e.cuda_event:  # torch creates the HIP event on its first record
                 e.record()
         ev = (ctypes.c_void_p * nchunks)(*[e.cuda_event for e in events])
+    wp, wn, _keep = _workspace("tp_row_linear_partial_chunked", (N, k_loc, n, nchunks), Z, stream, workspace)
     _check(lib.tp_row_linear_partial_chunked(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
-                                             nchunks, ev, _stream(stream)))
+                                             nchunks, ev, wp, wn, _stream(stream)))
     return P
 
 
 def tp_mlp_shard_fwd(X, W_in, W_out, act, Z=None, H_save=None, P=None, want_h=True,
-                     accumulate=False, stream=None):
+                     accumulate=False, workspace=None, stream=None):
     """One rank's MLP forward; returns (Z, H_save or None, P)."""
     lib = load()
     a = ACT[act]
@@ -207,14 +248,17 @@ def tp_mlp_shard_fwd(X, W_in, W_out, act, Z=None, H_save=None, P=None, want_h=Tr
     if H_save is not None:
         _dev(H_save, "H_save", _bf16, (N, n_w))
     P = _out(P, "P", _f32, (N, h), X)
+    wp, wn, _keep = _workspace("tp_mlp_shard_fwd", (N, h, f, a), X, stream, workspace)
     _check(lib.tp_mlp_shard_fwd(_ptr(X), _ptr(W_in), _ptr(W_out), N, h, f, a, _ptr(Z), _ptr(H_save),
-                                _ptr(P), int(bool(accumulate)), _stream(stream)))
+                                _ptr(P), int(bool(accumulate)), wp, wn, _stream(stream)))
     return Z, H_save, P
 
 
 def tp_mlp_shard_bwd(X, W_in, W_out, H_save, Z, dY, act, dH=None, dX_part=None, dW_in=None,
-                     dW_out=None, accumulate=False, stream=None):
-    """One rank's MLP backward; returns (dH, dX_part, dW_in, dW_out)."""
+                     dW_out=None, accumulate=False, want=("dX_part", "dW_in", "dW_out"), workspace=None,
+                     stream=None):
+    """One rank's MLP backward; returns (dH, dX_part, dW_in, dW_out). Outputs
+    not named in `want` are skipped (returned as None)."""
     lib = load()
     a = ACT[act]
     N, h = X.shape
@@ -226,18 +270,22 @@ def tp_mlp_shard_bwd(X, W_in, W_out, H_save, Z, dY, act, dH=None, dX_part=None, 
     _dev(H_save, "H_save", _bf16, (N, n_w))
     _dev(Z, "Z", _bf16, (N, f))
     _dev(dY, "dY", _bf16, (N, h))
+    unknown = set(want) - {"dX_part", "dW_in", "dW_out"}
+    if unknown:
+        raise ValueError(f"unknown outputs {sorted(unknown)}")
     dH = _out(dH, "dH", _bf16, (N, n_w), X)
-    dX_part = _out(dX_part, "dX_part", _f32, (N, h), X)
-    dW_in = _out(dW_in, "dW_in", _f32, (h, n_w), X)
-    dW_out = _out(dW_out, "dW_out", _f32, (f, h), X)
+    dX_part = _out(dX_part, "dX_part", _f32, (N, h), X) if "dX_part" in want else None
+    dW_in = _out(dW_in, "dW_in", _f32, (h, n_w), X) if "dW_in" in want else None
+    dW_out = _out(dW_out, "dW_out", _f32, (f, h), X) if "dW_out" in want else None
+    wp, wn, _keep = _workspace("tp_mlp_shard_bwd", (N, h, f, a), X, stream, workspace)
     _check(lib.tp_mlp_shard_bwd(_ptr(X), _ptr(W_in), _ptr(W_out), _ptr(H_save), _ptr(Z), _ptr(dY),
                                 N, h, f, a, _ptr(dH), _ptr(dX_part), _ptr(dW_in), _ptr(dW_out),
-                                int(bool(accumulate)), _stream(stream)))
+                                int(bool(accumulate)), wp, wn, _stream(stream)))
     return dH, dX_part, dW_in, dW_out
 
 
 def tp_col_linear_bwd(X, W, dY, dX_part=None, dW=None, want_dx=True, want_dw=True,
-                      accumulate=False, stream=None):
+                      accumulate=False, workspace=None, stream=None):
     """dX_part = dY W^T ({U}), dW = X^T dY; returns (dX_part, dW)."""
     lib = load()
     N, k = X.shape
@@ -249,13 +297,14 @@ def tp_col_linear_bwd(X, W, dY, dX_part=None, dW=None, want_dx=True, want_dw=Tru
         dX_part = _out(dX_part, "dX_part", _f32, (N, k), X)
     if want_dw:
         dW = _out(dW, "dW", _f32, (k, n), X)
+    wp, wn, _keep = _workspace("tp_col_linear_bwd", (N, k, n), X, stream, workspace)
     _check(lib.tp_col_linear_bwd(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX_part if want_dx else None),
-                                 _ptr(dW if want_dw else None), N, k, n, int(bool(accumulate)),
+                                 _ptr(dW if want_dw else None), N, k, n, int(bool(accumulate)), wp, wn,
                                  _stream(stream)))
     return (dX_part if want_dx else None), (dW if want_dw else None)
 
 
-def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, stream=None):
+def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, workspace=None, stream=None):
     """dZ = dY W^T (bf16), dW = Z^T dY (f32); returns (dZ, dW)."""
     lib = load()
     N, k_loc = Z.shape
@@ -267,8 +316,9 @@ def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, st
         dZ = _out(dZ, "dZ", _bf16, (N, k_loc), Z)
     if want_dw:
         dW = _out(dW, "dW", _f32, (k_loc, n), Z)
+    wp, wn, _keep = _workspace("tp_row_linear_bwd", (N, k_loc, n), Z, stream, workspace)
     _check(lib.tp_row_linear_bwd(_ptr(Z), _ptr(W), _ptr(dY), _ptr(dZ if want_dz else None),
-                                 _ptr(dW if want_dw else None), N, k_loc, n, _stream(stream)))
+                                 _ptr(dW if want_dw else None), N, k_loc, n, wp, wn, _stream(stream)))
     return (dZ if want_dz else None), (dW if want_dw else None)
 
 
@@ -309,7 +359,7 @@ def tp_kv_grad_accumulate(dW_dst, dW_src, n_h, n_kv, d_h, t, stream=None):
     return dW_dst
 
 
-def tp_vocab_ce_fwd(X, W_i, targets, vocab_start, stream=None):
+def tp_vocab_ce_fwd(X, W_i, targets, vocab_start, workspace=None, stream=None):
     """One rank's local cross-entropy statistics; returns (m_i, s_i, zy_i), f32 [N]."""
     lib = load()
     N, h = X.shape
@@ -318,8 +368,9 @@ def tp_vocab_ce_fwd(X, W_i, targets, vocab_start, stream=None):
     _dev(W_i, "W_i", _bf16, (h, v_loc))
     _dev(targets, "targets", torch.int32, (N,))
     m, s, zy = (torch.empty((N,), dtype=_f32, device=X.device) for _ in range(3))
+    wp, wn, _keep = _workspace("tp_vocab_ce_fwd", (N, h, v_loc), X, stream, workspace)
     _check(lib.tp_vocab_ce_fwd(_ptr(X), _ptr(W_i), _ptr(targets), vocab_start, N, h, v_loc, _ptr(m), _ptr(s),
-                               _ptr(zy), _stream(stream)))
+                               _ptr(zy), wp, wn, _stream(stream)))
     return m, s, zy
 
 
@@ -336,7 +387,7 @@ def tp_vocab_ce_combine(m_parts, s_parts, zy_parts, stream=None):
 
 
 def tp_vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss, dZ=None, dX_part=None, dW_i=None,
-                    accumulate=False, stream=None):
+                    accumulate=False, workspace=None, stream=None):
     """One rank's backward; returns (dZ, dX_part, dW_i)."""
     lib = load()
     N, h = X.shape
@@ -349,8 +400,9 @@ def tp_vocab_ce_bwd(X, W_i, targets, vocab_start, m, S, dloss, dZ=None, dX_part=
     dZ = _out(dZ, "dZ", _bf16, (N, v_loc), X)
     dX_part = _out(dX_part, "dX_part", _f32, (N, h), X)
     dW_i = _out(dW_i, "dW_i", _f32, (h, v_loc), X)
+    wp, wn, _keep = _workspace("tp_vocab_ce_bwd", (N, h, v_loc), X, stream, workspace)
     _check(lib.tp_vocab_ce_bwd(_ptr(X), _ptr(W_i), _ptr(targets), vocab_start, _ptr(m), _ptr(S), _ptr(dloss), N,
-                               h, v_loc, _ptr(dZ), _ptr(dX_part), _ptr(dW_i), int(bool(accumulate)),
+                               h, v_loc, _ptr(dZ), _ptr(dX_part), _ptr(dW_i), int(bool(accumulate)), wp, wn,
                                _stream(stream)))
     return dZ, dX_part, dW_i
 
@@ -371,14 +423,16 @@ def tp_vocab_embed_fwd(ids, E_i, vocab_start, out=None, accumulate=False, stream
     return out
 
 
-def tp_vocab_embed_bwd(ids, dY, vocab_start, v_loc, dE_i=None, stream=None):
+def tp_vocab_embed_bwd(ids, dY, vocab_start, v_loc, dE_i=None, workspace=None, stream=None):
     """Gradient of this rank's table rows; returns dE_i f32 [v_loc, h]."""
     lib = load()
     N, h = dY.shape
     _dev(ids, "ids", torch.int32, (N,))
     _dev(dY, "dY", _f32, (N, h))
     dE_i = _out(dE_i, "dE_i", _f32, (v_loc, h), dY)
-    _check(lib.tp_vocab_embed_bwd(_ptr(ids), _ptr(dY), vocab_start, N, v_loc, h, _ptr(dE_i), _stream(stream)))
+    wp, wn, _keep = _workspace("tp_vocab_embed_bwd", (N, v_loc, h), dY, stream, workspace)
+    _check(lib.tp_vocab_embed_bwd(_ptr(ids), _ptr(dY), vocab_start, N, v_loc, h, _ptr(dE_i), wp, wn,
+                                  _stream(stream)))
     return dE_i
 
 

@@ -119,46 +119,29 @@ static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, i
 // ---------------------------------------------------------------------------
 // Split-K. A product with too few output tiles for the CUs (decode-sized
 // token counts, or the narrow attention shards) has K split over workgroups:
-// each writes an fp32 partial of the whole product to a workspace, and
+// each writes an fp32 partial of the whole product to scratch memory, and
 // splitk_reduce sums the partials in split order and applies the epilogue
 // (store, accumulate, GeLU, SwiGLU). (Summing in the GEMM kernel by the last
 // workgroup of a tile needs device-scope fences, which write back and
 // invalidate each XCD's L2 for every workgroup: measured 1.5-3x slower.)
-// The workspace belongs to the library: one buffer per (device, stream),
-// grown on demand (hipMalloc outside any kernel; kept until the process
-// ends), so calls on different streams never share one.
+// The scratch belongs to the caller: every entry point that may need some
+// takes a device buffer and its size, and a host-only query gives the bytes
+// a call needs. The library allocates nothing, keeps no pointer and never
+// synchronises.
 // ---------------------------------------------------------------------------
-static std::mutex g_ws_mutex;
-static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+struct Workspace {
+    void* p;
+    size_t bytes;
+};
 
-static tp_status workspace(const char* fn, hipStream_t s, size_t bytes, float** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    auto& w = g_ws[{dev, s}];
-    if (w.second < bytes) {
-        // growing needs a stream synchronisation and hipMalloc, neither of
-        // which a stream under graph capture allows
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
-            return fail(TP_ERR_INVALID_ARG,
-                        "%s: the workspace of this stream must grow to %zu bytes while the stream is being "
-                        "captured; run the call once on the stream before capturing it",
-                        fn, bytes);
-        if (w.first) {
-            // earlier work on this stream may still read the old buffer
-            e = hipStreamSynchronize(s);
-            if (e == hipSuccess) e = hipFree(w.first);
-            if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: workspace release: %s", fn, hipGetErrorString(e));
-            w = {nullptr, 0};
-        }
-        void* p = nullptr;
-        e = hipMalloc(&p, bytes);
-        if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: workspace of %zu bytes: %s", fn, bytes, hipGetErrorString(e));
-        w = {p, bytes};
-    }
-    *out = static_cast<float*>(w.first);
+// The caller's workspace holds `need` bytes (checked before any launch).
+static tp_status check_workspace(const char* fn, const Workspace& ws, size_t need) {
+    if (ws.p != nullptr && !aligned16(ws.p))
+        return fail(TP_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+    if (need == 0) return TP_OK;
+    if (ws.p == nullptr || ws.bytes < need)
+        return fail(TP_ERR_INVALID_ARG, "%s: the call needs %zu bytes of workspace, got %zu%s", fn, need,
+                    ws.p ? ws.bytes : (size_t)0, ws.p ? "" : " (NULL)");
     return TP_OK;
 }
 
@@ -334,25 +317,23 @@ static SplitPlan plan_of(const GemmArgs& a) {
     return plan_split(a, EPI == EPI_SWIGLU, !A_T && B_KN, reducible<EPI>());
 }
 
-// Takes the stream's workspace for the largest of a call's plans before the
-// call enqueues anything, so that a failed allocation leaves nothing behind.
-static tp_status reserve(const char* fn, hipStream_t s, std::initializer_list<SplitPlan> plans) {
+// Workspace bytes of a call that runs several products one after another on
+// its stream (they reuse one buffer): the largest of their plans.
+static size_t need_of(std::initializer_list<SplitPlan> plans) {
     size_t bytes = 0;
     for (const SplitPlan& p : plans) bytes = std::max(bytes, p.bytes);
-    if (bytes == 0) return TP_OK;
-    float* ws = nullptr;
-    return workspace(fn, s, bytes, &ws);
+    return bytes;
 }
 
-// A product with its epilogue, run as plan_of decides.
+// A product with its epilogue, run as plan_of decides; a split product puts
+// its partials in ws (sized by the caller from the same plan).
 template <bool A_T, bool B_KN, int EPI>
-static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
+static tp_status run_gemm(const char* fn, const GemmArgs& a, void* ws, hipStream_t s) {
     if (a.M == 0 || a.N == 0) return TP_OK;
     const SplitPlan plan = plan_of<A_T, B_KN, EPI>(a);
     if (plan.ksplit == 0) return launch_gemm<A_T, B_KN, EPI>(fn, a, s);
     if constexpr (reducible<EPI>()) {
-        float* ws = nullptr;
-        TP_TRY(workspace(fn, s, plan.bytes, &ws));
+        if (ws == nullptr) return fail(TP_ERR_INVALID_ARG, "%s: a split product without workspace", fn);
         GemmArgs p = a;
         p.C = ws;
         p.ldc = plan.Nw;
@@ -367,8 +348,8 @@ static tp_status run_gemm(const char* fn, const GemmArgs& a, hipStream_t s) {
         const long long quads = (long long)a.M * (a.N / 4);
         const long long per_block = 4 * (64 / S);
         const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
-        hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, ws, plan.ksplit, S, a.M,
-                           plan.Nw, a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
+        hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(ws),
+                           plan.ksplit, S, a.M, plan.Nw, a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
         return TP_OK;
@@ -629,97 +610,331 @@ __global__ void __launch_bounds__(256) qkv_regroup_kernel(const uint16_t* __rest
 
 }  // namespace tps
 
-using namespace tps;
+// ---------------------------------------------------------------------------
+// Each entry point that runs GEMMs first validates its sizes and describes
+// its products (pointers may be NULL here: the host-only workspace queries
+// run the same code), giving the workspace bytes its split products need.
+// ---------------------------------------------------------------------------
+namespace tps {
 
-extern "C" {
+static tp_status check_act(const char* fn, int act, bool allow_none) {
+    if ((allow_none && act == TP_ACT_NONE) || act == TP_ACT_GELU || act == TP_ACT_SWIGLU) return TP_OK;
+    if (!allow_none && act == TP_ACT_NONE)
+        return fail(TP_ERR_INVALID_ARG, "%s: act must be GELU or SWIGLU (got %d)", fn, act);
+    return fail(TP_ERR_INVALID_ARG, "%s: unknown act %d", fn, act);
+}
 
-int tp_version(void) { return (0 << 16) | 1; }
-
-const char* tp_last_error(void) { return g_last_error.c_str(); }
-
-tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_t k, int64_t n_out,
-                        int act, void* H_save, void* stream) {
-    const char* fn = "tp_col_linear";
+static tp_status col_linear_plan(const char* fn, const void* X, const void* W, void* Y, int64_t N, int64_t k,
+                                 int64_t n_out, int act, void* H_save, GemmArgs& a, size_t& need) {
     TP_TRY(check_tokens(fn, N));
     TP_TRY(check_width(fn, "k", k));
     TP_TRY(check_width(fn, "n_out", n_out));
-    if (act != TP_ACT_NONE && act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
-        return fail(TP_ERR_INVALID_ARG, "%s: unknown act %d", fn, act);
+    TP_TRY(check_act(fn, act, true));
     if (act == TP_ACT_NONE && H_save != nullptr)
         return fail(TP_ERR_INVALID_ARG, "%s: H_save must be NULL for act NONE", fn);
-    TP_CHECK_TOK_PTR(X, "X");
-    TP_CHECK_PTR(W, "W");
-    TP_CHECK_TOK_PTR(Y, "Y");
-    TP_CHECK_OPT_PTR(H_save, "H_save");
     const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * n_out : n_out;
     TP_TRY(check_elems(fn, N, k));
     TP_TRY(check_elems(fn, k, n_w));
     TP_TRY(check_elems(fn, N, n_w));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    GemmArgs a = make_args(X, W, Y, (int)N, (int)n_out, (int)k, (int)k, (int)n_w, (int)n_out);
+    a = make_args(X, W, Y, (int)N, (int)n_out, (int)k, (int)k, (int)n_w, (int)n_out);
     a.C2 = static_cast<uint16_t*>(H_save);
     a.ldc2 = (int)n_w;
     a.f = (int)n_out;
-    tp_status st;
-    if (act == TP_ACT_NONE) st = run_gemm<false, true, EPI_BF16>(fn, a, s);
-    else if (act == TP_ACT_GELU) st = run_gemm<false, true, EPI_GELU>(fn, a, s);
-    else st = run_gemm<false, true, EPI_SWIGLU>(fn, a, s);
-    return st == TP_OK ? ok() : st;
+    need = act == TP_ACT_NONE   ? plan_of<false, true, EPI_BF16>(a).bytes
+           : act == TP_ACT_GELU ? plan_of<false, true, EPI_GELU>(a).bytes
+                                : plan_of<false, true, EPI_SWIGLU>(a).bytes;
+    return TP_OK;
 }
 
-tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc, int64_t n,
-                                int accumulate, void* stream) {
-    const char* fn = "tp_row_linear_partial";
+static tp_status col_linear_run(const char* fn, const GemmArgs& a, int act, void* ws, hipStream_t s) {
+    if (act == TP_ACT_NONE) return run_gemm<false, true, EPI_BF16>(fn, a, ws, s);
+    if (act == TP_ACT_GELU) return run_gemm<false, true, EPI_GELU>(fn, a, ws, s);
+    return run_gemm<false, true, EPI_SWIGLU>(fn, a, ws, s);
+}
+
+static tp_status row_partial_plan(const char* fn, const void* Z, const void* W, float* P, int64_t N,
+                                  int64_t k_loc, int64_t n, int accumulate, GemmArgs& a, size_t& need) {
     TP_TRY(check_tokens(fn, N));
     TP_TRY(check_width(fn, "k_loc", k_loc));
     TP_TRY(check_width(fn, "n", n));
-    TP_CHECK_TOK_PTR(Z, "Z");
-    TP_CHECK_PTR(W, "W");
-    TP_CHECK_TOK_PTR(P, "P");
     TP_TRY(check_elems(fn, N, k_loc));
     TP_TRY(check_elems(fn, k_loc, n));
     TP_TRY(check_elems(fn, N, n));
-    GemmArgs a = make_args(Z, W, P, (int)N, (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
+    a = make_args(Z, W, P, (int)N, (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
     a.accumulate = accumulate ? 1 : 0;
-    tp_status st = run_gemm<false, true, EPI_F32>(fn, a, static_cast<hipStream_t>(stream));
-    return st == TP_OK ? ok() : st;
+    need = plan_of<false, true, EPI_F32>(a).bytes;
+    return TP_OK;
 }
 
-tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc,
-                                        int64_t n, int accumulate, int32_t nchunks, void* const* events,
-                                        void* stream) {
-    const char* fn = "tp_row_linear_partial_chunked";
+// chunk c of the chunked row partial: token rows [c rows, (c + 1) rows),
+// rows = ceil(N / nchunks) rounded up to 16
+static GemmArgs row_chunk(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc, int64_t n,
+                          int accumulate, int nchunks, int c) {
+    const int64_t rows = ((N + nchunks - 1) / nchunks + 15) / 16 * 16;
+    const int64_t r0 = std::min<int64_t>(N, c * rows), r1 = std::min<int64_t>(N, r0 + rows);
+    GemmArgs a = make_args(Z ? static_cast<const uint16_t*>(Z) + r0 * k_loc : nullptr, W, P ? P + r0 * n : nullptr,
+                           (int)(r1 - r0), (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
+    a.accumulate = accumulate ? 1 : 0;
+    return a;
+}
+
+static tp_status row_chunked_plan(const char* fn, int64_t N, int64_t k_loc, int64_t n, int32_t nchunks,
+                                  size_t& need) {
     TP_TRY(check_tokens(fn, N));
     TP_TRY(check_width(fn, "k_loc", k_loc));
     TP_TRY(check_width(fn, "n", n));
     if (nchunks < 1 || nchunks > 64) return fail(TP_ERR_INVALID_ARG, "%s: nchunks = %d outside [1, 64]", fn, nchunks);
-    TP_CHECK_TOK_PTR(Z, "Z");
-    TP_CHECK_PTR(W, "W");
-    TP_CHECK_TOK_PTR(P, "P");
     TP_TRY(check_elems(fn, N, k_loc));
     TP_TRY(check_elems(fn, k_loc, n));
     TP_TRY(check_elems(fn, N, n));
+    need = 0;  // the chunks run one after another and reuse one workspace
+    for (int c = 0; c < nchunks; ++c)
+        need = std::max(need, plan_of<false, true, EPI_F32>(row_chunk(nullptr, nullptr, nullptr, N, k_loc, n, 0,
+                                                                       nchunks, c)).bytes);
+    return TP_OK;
+}
+
+static tp_status mlp_fwd_plan(const char* fn, const void* X, const void* W_in, const void* W_out, int64_t N,
+                              int64_t h, int64_t f, int act, void* Z, void* H_save, float* P, int accumulate,
+                              GemmArgs& a, GemmArgs& b, size_t& need) {
+    TP_TRY(check_act(fn, act, false));
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "f", f));
+    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, n_w));
+    TP_TRY(check_elems(fn, N, n_w));
+    a = make_args(X, W_in, Z, (int)N, (int)f, (int)h, (int)h, (int)n_w, (int)f);
+    a.C2 = static_cast<uint16_t*>(H_save);
+    a.ldc2 = (int)n_w;
+    a.f = (int)f;
+    b = make_args(Z, W_out, P, (int)N, (int)h, (int)f, (int)f, (int)h, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    need = need_of({act == TP_ACT_GELU ? plan_of<false, true, EPI_GELU>(a) : plan_of<false, true, EPI_SWIGLU>(a),
+                    plan_of<false, true, EPI_F32>(b)});
+    return TP_OK;
+}
+
+// The backward's products: a = dZ with the activation backward -> dH (NT),
+// b = dX_part (NT), c = dW_in (TN), d = dW_out (TN); a product whose output
+// is NULL is not run (its workspace is not counted).
+static tp_status mlp_bwd_plan(const char* fn, const void* X, const void* W_in, const void* W_out,
+                              const void* H_save, const void* Z, const void* dY, int64_t N, int64_t h, int64_t f,
+                              int act, void* dH, float* dX_part, float* dW_in, float* dW_out, int accumulate,
+                              bool query, GemmArgs& a, GemmArgs& b, GemmArgs& c, GemmArgs& d, size_t& need) {
+    TP_TRY(check_act(fn, act, false));
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "f", f));
+    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, n_w));
+    TP_TRY(check_elems(fn, N, n_w));
+    // dZ = dY W_out^T (NT) with the activation backward in the epilogue -> dH
+    a = make_args(dY, W_out, dH, (int)N, (int)f, (int)h, (int)h, (int)h, (int)n_w);
+    a.aux = static_cast<const uint16_t*>(H_save);
+    a.ldc2 = (int)n_w;
+    a.f = (int)f;
+    // dX_part = dH W_in^T (NT)
+    b = make_args(dH, W_in, dX_part, (int)N, (int)h, (int)n_w, (int)n_w, (int)n_w, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    // dW_in = X^T dH (TN): A = X stored [K=N][M=h], B = dH stored [K=N][n_w]
+    c = make_args(X, dH, dW_in, (int)h, (int)n_w, (int)N, (int)h, (int)n_w, (int)n_w);
+    // dW_out = Z^T dY (TN): A = Z stored [N][f], B = dY stored [N][h]
+    d = make_args(Z, dY, dW_out, (int)f, (int)h, (int)N, (int)f, (int)h, (int)h);
+    need = need_of({(query || dX_part) ? plan_of<false, false, EPI_F32>(b) : SplitPlan{},
+                    (query || dW_in) ? plan_of<true, true, EPI_F32>(c) : SplitPlan{},
+                    (query || dW_out) ? plan_of<true, true, EPI_F32>(d) : SplitPlan{}});
+    return TP_OK;
+}
+
+static tp_status col_bwd_plan(const char* fn, const void* X, const void* W, const void* dY, float* dX_part,
+                              float* dW, int64_t N, int64_t k, int64_t n, int accumulate, bool query, GemmArgs& a,
+                              GemmArgs& b, size_t& need) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k", k));
+    TP_TRY(check_width(fn, "n", n));
+    TP_TRY(check_elems(fn, N, k));
+    TP_TRY(check_elems(fn, k, n));
+    TP_TRY(check_elems(fn, N, n));
+    a = make_args(dY, W, dX_part, (int)N, (int)k, (int)n, (int)n, (int)n, (int)k);
+    a.accumulate = accumulate ? 1 : 0;
+    b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
+    need = need_of({(query || dX_part) ? plan_of<false, false, EPI_F32>(a) : SplitPlan{},
+                    (query || dW) ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}});
+    return TP_OK;
+}
+
+static tp_status row_bwd_plan(const char* fn, const void* Z, const void* W, const void* dY, void* dZ, float* dW,
+                              int64_t N, int64_t k_loc, int64_t n, bool query, GemmArgs& a, GemmArgs& b,
+                              size_t& need) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "k_loc", k_loc));
+    TP_TRY(check_width(fn, "n", n));
+    TP_TRY(check_elems(fn, N, k_loc));
+    TP_TRY(check_elems(fn, k_loc, n));
+    TP_TRY(check_elems(fn, N, n));
+    a = make_args(dY, W, dZ, (int)N, (int)k_loc, (int)n, (int)n, (int)n, (int)k_loc);
+    b = make_args(Z, dY, dW, (int)k_loc, (int)n, (int)N, (int)k_loc, (int)n, (int)n);
+    need = need_of({(query || dZ) ? plan_of<false, false, EPI_BF16>(a) : SplitPlan{},
+                    (query || dW) ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}});
+    return TP_OK;
+}
+
+// Common checks of the vocab-parallel cross-entropy calls.
+static tp_status check_ce(const char* fn, int64_t N, int64_t h, int64_t v_loc, int64_t vocab_start) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    TP_TRY(check_width(fn, "v_loc", v_loc));
+    if (vocab_start < 0 || vocab_start + v_loc > 0x7fffffffLL)
+        return fail(TP_ERR_INVALID_ARG, "%s: vocab range [%lld, %lld) outside int32", fn, (long long)vocab_start,
+                    (long long)(vocab_start + v_loc));
+    TP_TRY(check_elems(fn, N, h));
+    TP_TRY(check_elems(fn, h, v_loc));
+    TP_TRY(check_elems(fn, N, v_loc));
+    return TP_OK;
+}
+
+static tp_status check_targets(const char* fn, int64_t N, const int32_t* targets) {
+    if (N > 0 && (targets == nullptr || (reinterpret_cast<uintptr_t>(targets) & 3u)))
+        return fail(TP_ERR_INVALID_ARG, "%s: targets is NULL or not 4-byte aligned", fn);
+    return TP_OK;
+}
+
+// records: 2 wave column blocks per kCeTileN-wide tile (launch_gemm runs
+// EPI_CE_STATS with 256 x 224 tiles of 2 x 2 waves), 3 floats each per row
+static int ce_parts(int64_t v_loc) { return (int)(2 * ((v_loc + kCeTileN - 1) / kCeTileN)); }
+static size_t ce_fwd_need(int64_t N, int64_t v_loc) { return (size_t)N * ce_parts(v_loc) * 3 * sizeof(float); }
+
+static void ce_bwd_args(const void* X, const void* W_i, void* dZ, float* dX_part, float* dW_i, int64_t N, int64_t h,
+                        int64_t v_loc, int accumulate, GemmArgs& b, GemmArgs& c) {
+    // dX_part = dZ W_i^T (NT, {U}); dW_i = X^T dZ (TN)
+    b = make_args(dZ, W_i, dX_part, (int)N, (int)h, (int)v_loc, (int)v_loc, (int)v_loc, (int)h);
+    b.accumulate = accumulate ? 1 : 0;
+    c = make_args(X, dZ, dW_i, (int)h, (int)v_loc, (int)N, (int)h, (int)v_loc, (int)v_loc);
+}
+
+static size_t ce_bwd_need(const GemmArgs& b, const GemmArgs& c) {
+    return need_of({plan_of<false, false, EPI_F32>(b), plan_of<true, true, EPI_F32>(c)});
+}
+
+static tp_status check_embed(const char* fn, int64_t N, int64_t v_loc, int64_t h, int64_t vocab_start) {
+    TP_TRY(check_tokens(fn, N));
+    TP_TRY(check_width(fn, "h", h));
+    if (v_loc <= 0 || v_loc > 0x7fffffffLL) return fail(TP_ERR_INVALID_ARG, "%s: v_loc = %lld", fn, (long long)v_loc);
+    if (vocab_start < 0) return fail(TP_ERR_INVALID_ARG, "%s: vocab_start < 0", fn);
+    TP_TRY(check_elems(fn, v_loc, h));
+    TP_TRY(check_elems(fn, N, h));
+    return TP_OK;
+}
+
+static tp_status check_ids(const char* fn, int64_t N, const int32_t* ids) {
+    if (N > 0 && (ids == nullptr || (reinterpret_cast<uintptr_t>(ids) & 3u)))
+        return fail(TP_ERR_INVALID_ARG, "%s: ids is NULL or not 4-byte aligned", fn);
+    return TP_OK;
+}
+
+static tp_status embed_bwd_plan(const char* fn, int64_t N, int64_t v_loc, int64_t h, int64_t vocab_start,
+                                size_t& need) {
+    TP_TRY(check_embed(fn, N, v_loc, h, vocab_start));
+    if (h > kEmbedMaxH) return fail(TP_ERR_UNSUPPORTED, "%s: h = %lld above %d", fn, (long long)h, kEmbedMaxH);
+    if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    need = (size_t)v_loc * sizeof(uint32_t);  // one stamp per table row
+    return TP_OK;
+}
+
+}  // namespace tps
+
+using namespace tps;
+
+#define TP_QUERY_OUT(p)                                                                 \
+    do {                                                                                \
+        if ((p) == nullptr) return fail(TP_ERR_INVALID_ARG, "%s: bytes is NULL", fn);   \
+    } while (0)
+
+extern "C" {
+
+int tp_version(void) { return (0 << 16) | 2; }
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+tp_status tp_col_linear_workspace_size(int64_t N, int64_t k, int64_t n_out, int act, size_t* bytes) {
+    const char* fn = "tp_col_linear_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a;
+    size_t need = 0;
+    TP_TRY(col_linear_plan(fn, nullptr, nullptr, nullptr, N, k, n_out, act, nullptr, a, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_t k, int64_t n_out, int act,
+                        void* H_save, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "tp_col_linear";
+    GemmArgs a;
+    size_t need = 0;
+    TP_TRY(col_linear_plan(fn, X, W, Y, N, k, n_out, act, H_save, a, need));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(Y, "Y");
+    TP_CHECK_OPT_PTR(H_save, "H_save");
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
+    TP_TRY(col_linear_run(fn, a, act, workspace, static_cast<hipStream_t>(stream)));
+    return ok();
+}
+
+tp_status tp_row_linear_partial_workspace_size(int64_t N, int64_t k_loc, int64_t n, size_t* bytes) {
+    const char* fn = "tp_row_linear_partial_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a;
+    size_t need = 0;
+    TP_TRY(row_partial_plan(fn, nullptr, nullptr, nullptr, N, k_loc, n, 0, a, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_row_linear_partial(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc, int64_t n,
+                                int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "tp_row_linear_partial";
+    GemmArgs a;
+    size_t need = 0;
+    TP_TRY(row_partial_plan(fn, Z, W, P, N, k_loc, n, accumulate, a, need));
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(P, "P");
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
+    TP_TRY((run_gemm<false, true, EPI_F32>(fn, a, workspace, static_cast<hipStream_t>(stream))));
+    return ok();
+}
+
+tp_status tp_row_linear_partial_chunked_workspace_size(int64_t N, int64_t k_loc, int64_t n, int32_t nchunks,
+                                                       size_t* bytes) {
+    const char* fn = "tp_row_linear_partial_chunked_workspace_size";
+    TP_QUERY_OUT(bytes);
+    size_t need = 0;
+    TP_TRY(row_chunked_plan(fn, N, k_loc, n, nchunks, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc,
+                                        int64_t n, int accumulate, int32_t nchunks, void* const* events,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "tp_row_linear_partial_chunked";
+    size_t need = 0;
+    TP_TRY(row_chunked_plan(fn, N, k_loc, n, nchunks, need));
+    TP_CHECK_TOK_PTR(Z, "Z");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(P, "P");
     if (events)
         for (int c = 0; c < nchunks; ++c)
             if (!events[c]) return fail(TP_ERR_INVALID_ARG, "%s: events[%d] is NULL", fn, c);
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // chunk c: token rows [c rows, (c + 1) rows), rows a multiple of 16
-    const int64_t rows = ((N + nchunks - 1) / nchunks + 15) / 16 * 16;
-    auto chunk = [&](int c) {
-        const int64_t r0 = std::min<int64_t>(N, c * rows), r1 = std::min<int64_t>(N, r0 + rows);
-        GemmArgs a = make_args(static_cast<const uint16_t*>(Z) + r0 * k_loc, W, P + r0 * n, (int)(r1 - r0), (int)n,
-                               (int)k_loc, (int)k_loc, (int)n, (int)n);
-        a.accumulate = accumulate ? 1 : 0;
-        return a;
-    };
-    size_t ws = 0;
-    for (int c = 0; c < nchunks; ++c) ws = std::max(ws, plan_of<false, true, EPI_F32>(chunk(c)).bytes);
-    if (ws) {
-        float* p = nullptr;
-        TP_TRY(workspace(fn, s, ws, &p));
-    }
     for (int c = 0; c < nchunks; ++c) {
-        TP_TRY((run_gemm<false, true, EPI_F32>(fn, chunk(c), s)));
+        TP_TRY((run_gemm<false, true, EPI_F32>(fn, row_chunk(Z, W, P, N, k_loc, n, accumulate, nchunks, c),
+                                               workspace, s)));
         if (events) {
             hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[c]), s);
             if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: event %d: %s", fn, c, hipGetErrorString(e));
@@ -728,143 +943,131 @@ tp_status tp_row_linear_partial_chunked(const void* Z, const void* W, float* P, 
     return ok();
 }
 
-tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, int64_t N, int64_t h,
-                           int64_t f, int act, void* Z, void* H_save, float* P, int accumulate,
-                           void* stream) {
+tp_status tp_mlp_shard_fwd_workspace_size(int64_t N, int64_t h, int64_t f, int act, size_t* bytes) {
+    const char* fn = "tp_mlp_shard_fwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(mlp_fwd_plan(fn, nullptr, nullptr, nullptr, N, h, f, act, nullptr, nullptr, nullptr, 0, a, b, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_mlp_shard_fwd(const void* X, const void* W_in, const void* W_out, int64_t N, int64_t h, int64_t f,
+                           int act, void* Z, void* H_save, float* P, int accumulate, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     const char* fn = "tp_mlp_shard_fwd";
-    if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
-        return fail(TP_ERR_INVALID_ARG, "%s: act must be GELU or SWIGLU (got %d)", fn, act);
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "h", h));
-    TP_TRY(check_width(fn, "f", f));
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(mlp_fwd_plan(fn, X, W_in, W_out, N, h, f, act, Z, H_save, P, accumulate, a, b, need));
     TP_CHECK_TOK_PTR(X, "X");
     TP_CHECK_PTR(W_in, "W_in");
     TP_CHECK_PTR(W_out, "W_out");
     TP_CHECK_TOK_PTR(Z, "Z");
     TP_CHECK_TOK_PTR(P, "P");
     TP_CHECK_OPT_PTR(H_save, "H_save");
-    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
-    TP_TRY(check_elems(fn, N, h));
-    TP_TRY(check_elems(fn, h, n_w));
-    TP_TRY(check_elems(fn, N, n_w));
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    GemmArgs a = make_args(X, W_in, Z, (int)N, (int)f, (int)h, (int)h, (int)n_w, (int)f);
-    a.C2 = static_cast<uint16_t*>(H_save);
-    a.ldc2 = (int)n_w;
-    a.f = (int)f;
-    GemmArgs b = make_args(Z, W_out, P, (int)N, (int)h, (int)f, (int)f, (int)h, (int)h);
-    b.accumulate = accumulate ? 1 : 0;
-    // both products share the stream's workspace: size it for the larger
-    // before the first launch, so a failed allocation enqueues nothing
-    TP_TRY(reserve(fn, s,
-                   {act == TP_ACT_GELU ? plan_of<false, true, EPI_GELU>(a) : plan_of<false, true, EPI_SWIGLU>(a),
-                    plan_of<false, true, EPI_F32>(b)}));
-    tp_status st = act == TP_ACT_GELU ? run_gemm<false, true, EPI_GELU>(fn, a, s)
-                                      : run_gemm<false, true, EPI_SWIGLU>(fn, a, s);
-    if (st != TP_OK) return st;
-    st = run_gemm<false, true, EPI_F32>(fn, b, s);
-    return st == TP_OK ? ok() : st;
+    TP_TRY((act == TP_ACT_GELU ? run_gemm<false, true, EPI_GELU>(fn, a, workspace, s)
+                               : run_gemm<false, true, EPI_SWIGLU>(fn, a, workspace, s)));
+    TP_TRY((run_gemm<false, true, EPI_F32>(fn, b, workspace, s)));
+    return ok();
 }
 
-tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out, const void* H_save,
-                           const void* Z, const void* dY, int64_t N, int64_t h, int64_t f, int act,
-                           void* dH, float* dX_part, float* dW_in, float* dW_out, int accumulate,
+tp_status tp_mlp_shard_bwd_workspace_size(int64_t N, int64_t h, int64_t f, int act, size_t* bytes) {
+    const char* fn = "tp_mlp_shard_bwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a, b, c, d;
+    size_t need = 0;
+    TP_TRY(mlp_bwd_plan(fn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, N, h, f, act, nullptr, nullptr,
+                        nullptr, nullptr, 0, true, a, b, c, d, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_mlp_shard_bwd(const void* X, const void* W_in, const void* W_out, const void* H_save, const void* Z,
+                           const void* dY, int64_t N, int64_t h, int64_t f, int act, void* dH, float* dX_part,
+                           float* dW_in, float* dW_out, int accumulate, void* workspace, size_t workspace_bytes,
                            void* stream) {
     const char* fn = "tp_mlp_shard_bwd";
-    if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
-        return fail(TP_ERR_INVALID_ARG, "%s: act must be GELU or SWIGLU (got %d)", fn, act);
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "h", h));
-    TP_TRY(check_width(fn, "f", f));
-    TP_CHECK_TOK_PTR(X, "X");
-    TP_CHECK_PTR(W_in, "W_in");
+    GemmArgs a, b, c, d;
+    size_t need = 0;
+    TP_TRY(mlp_bwd_plan(fn, X, W_in, W_out, H_save, Z, dY, N, h, f, act, dH, dX_part, dW_in, dW_out, accumulate,
+                        false, a, b, c, d, need));
     TP_CHECK_PTR(W_out, "W_out");
     TP_CHECK_TOK_PTR(H_save, "H_save");
-    TP_CHECK_TOK_PTR(Z, "Z");
     TP_CHECK_TOK_PTR(dY, "dY");
     TP_CHECK_TOK_PTR(dH, "dH");
-    TP_CHECK_TOK_PTR(dX_part, "dX_part");
-    TP_CHECK_PTR(dW_in, "dW_in");
-    TP_CHECK_PTR(dW_out, "dW_out");
-    const int64_t n_w = act == TP_ACT_SWIGLU ? 2 * f : f;
-    TP_TRY(check_elems(fn, N, h));
-    TP_TRY(check_elems(fn, h, n_w));
-    TP_TRY(check_elems(fn, N, n_w));
+    TP_CHECK_OPT_PTR(dX_part, "dX_part");
+    TP_CHECK_OPT_PTR(dW_in, "dW_in");
+    TP_CHECK_OPT_PTR(dW_out, "dW_out");
+    if (dX_part) TP_CHECK_PTR(W_in, "W_in");
+    if (dW_in) TP_CHECK_TOK_PTR(X, "X");
+    if (dW_out) TP_CHECK_TOK_PTR(Z, "Z");
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // dZ = dY W_out^T (NT) with the activation backward in the epilogue -> dH
-    GemmArgs a = make_args(dY, W_out, dH, (int)N, (int)f, (int)h, (int)h, (int)h, (int)n_w);
-    a.aux = static_cast<const uint16_t*>(H_save);
-    a.ldc2 = (int)n_w;
-    a.f = (int)f;
-    // dX_part = dH W_in^T (NT)
-    GemmArgs b = make_args(dH, W_in, dX_part, (int)N, (int)h, (int)n_w, (int)n_w, (int)n_w, (int)h);
-    b.accumulate = accumulate ? 1 : 0;
-    // dW_in = X^T dH (TN): A = X stored [K=N][M=h], B = dH stored [K=N][n_w]
-    GemmArgs c = make_args(X, dH, dW_in, (int)h, (int)n_w, (int)N, (int)h, (int)n_w, (int)n_w);
-    // dW_out = Z^T dY (TN): A = Z stored [N][f], B = dY stored [N][h]
-    GemmArgs d = make_args(Z, dY, dW_out, (int)f, (int)h, (int)N, (int)f, (int)h, (int)h);
-    TP_TRY(reserve(fn, s,
-                   {plan_of<false, false, EPI_F32>(b), plan_of<true, true, EPI_F32>(c),
-                    plan_of<true, true, EPI_F32>(d)}));
-    tp_status st = act == TP_ACT_GELU ? launch_gemm<false, false, EPI_GELU_BWD>(fn, a, s)
-                                      : launch_gemm<false, false, EPI_SWIGLU_BWD>(fn, a, s);
-    if (st != TP_OK) return st;
-    st = run_gemm<false, false, EPI_F32>(fn, b, s);
-    if (st != TP_OK) return st;
-    st = run_gemm<true, true, EPI_F32>(fn, c, s);
-    if (st != TP_OK) return st;
-    st = run_gemm<true, true, EPI_F32>(fn, d, s);
-    return st == TP_OK ? ok() : st;
+    TP_TRY((act == TP_ACT_GELU ? launch_gemm<false, false, EPI_GELU_BWD>(fn, a, s)
+                               : launch_gemm<false, false, EPI_SWIGLU_BWD>(fn, a, s)));
+    if (dX_part) TP_TRY((run_gemm<false, false, EPI_F32>(fn, b, workspace, s)));
+    if (dW_in) TP_TRY((run_gemm<true, true, EPI_F32>(fn, c, workspace, s)));
+    if (dW_out) TP_TRY((run_gemm<true, true, EPI_F32>(fn, d, workspace, s)));
+    return ok();
 }
 
-tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY, float* dX_part, float* dW,
-                            int64_t N, int64_t k, int64_t n, int accumulate, void* stream) {
+tp_status tp_col_linear_bwd_workspace_size(int64_t N, int64_t k, int64_t n, size_t* bytes) {
+    const char* fn = "tp_col_linear_bwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(col_bwd_plan(fn, nullptr, nullptr, nullptr, nullptr, nullptr, N, k, n, 0, true, a, b, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY, float* dX_part, float* dW, int64_t N,
+                            int64_t k, int64_t n, int accumulate, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     const char* fn = "tp_col_linear_bwd";
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "k", k));
-    TP_TRY(check_width(fn, "n", n));
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(col_bwd_plan(fn, X, W, dY, dX_part, dW, N, k, n, accumulate, false, a, b, need));
     TP_CHECK_TOK_PTR(dY, "dY");
     TP_CHECK_OPT_PTR(dX_part, "dX_part");
     TP_CHECK_OPT_PTR(dW, "dW");
     if (dX_part) TP_CHECK_PTR(W, "W");
     if (dW) TP_CHECK_TOK_PTR(X, "X");
-    TP_TRY(check_elems(fn, N, k));
-    TP_TRY(check_elems(fn, k, n));
-    TP_TRY(check_elems(fn, N, n));
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    GemmArgs a = make_args(dY, W, dX_part, (int)N, (int)k, (int)n, (int)n, (int)n, (int)k);
-    a.accumulate = accumulate ? 1 : 0;
-    GemmArgs b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
-    TP_TRY(reserve(fn, s,
-                   {dX_part ? plan_of<false, false, EPI_F32>(a) : SplitPlan{},
-                    dW ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}}));
-    if (dX_part) TP_TRY((run_gemm<false, false, EPI_F32>(fn, a, s)));
-    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, s)));
+    if (dX_part) TP_TRY((run_gemm<false, false, EPI_F32>(fn, a, workspace, s)));
+    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, workspace, s)));
+    return ok();
+}
+
+tp_status tp_row_linear_bwd_workspace_size(int64_t N, int64_t k_loc, int64_t n, size_t* bytes) {
+    const char* fn = "tp_row_linear_bwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(row_bwd_plan(fn, nullptr, nullptr, nullptr, nullptr, nullptr, N, k_loc, n, true, a, b, need));
+    *bytes = need;
     return ok();
 }
 
 tp_status tp_row_linear_bwd(const void* Z, const void* W, const void* dY, void* dZ, float* dW, int64_t N,
-                            int64_t k_loc, int64_t n, void* stream) {
+                            int64_t k_loc, int64_t n, void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "tp_row_linear_bwd";
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "k_loc", k_loc));
-    TP_TRY(check_width(fn, "n", n));
+    GemmArgs a, b;
+    size_t need = 0;
+    TP_TRY(row_bwd_plan(fn, Z, W, dY, dZ, dW, N, k_loc, n, false, a, b, need));
     TP_CHECK_TOK_PTR(dY, "dY");
     TP_CHECK_OPT_PTR(dZ, "dZ");
     TP_CHECK_OPT_PTR(dW, "dW");
     if (dZ) TP_CHECK_PTR(W, "W");
     if (dW) TP_CHECK_TOK_PTR(Z, "Z");
-    TP_TRY(check_elems(fn, N, k_loc));
-    TP_TRY(check_elems(fn, k_loc, n));
-    TP_TRY(check_elems(fn, N, n));
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    GemmArgs a = make_args(dY, W, dZ, (int)N, (int)k_loc, (int)n, (int)n, (int)n, (int)k_loc);
-    GemmArgs b = make_args(Z, dY, dW, (int)k_loc, (int)n, (int)N, (int)k_loc, (int)n, (int)n);
-    TP_TRY(reserve(fn, s,
-                   {dZ ? plan_of<false, false, EPI_BF16>(a) : SplitPlan{},
-                    dW ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}}));
-    if (dZ) TP_TRY((run_gemm<false, false, EPI_BF16>(fn, a, s)));
-    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, s)));
+    if (dZ) TP_TRY((run_gemm<false, false, EPI_BF16>(fn, a, workspace, s)));
+    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, workspace, s)));
     return ok();
 }
 
@@ -940,39 +1143,30 @@ tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h, i
     return ok();
 }
 
-// Common checks of the vocab-parallel cross-entropy calls.
-static tp_status check_ce(const char* fn, int64_t N, int64_t h, int64_t v_loc, int64_t vocab_start,
-                          const int32_t* targets) {
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "h", h));
-    TP_TRY(check_width(fn, "v_loc", v_loc));
-    if (vocab_start < 0 || vocab_start + v_loc > 0x7fffffffLL)
-        return fail(TP_ERR_INVALID_ARG, "%s: vocab range [%lld, %lld) outside int32", fn, (long long)vocab_start,
-                    (long long)(vocab_start + v_loc));
-    if (N > 0 && (targets == nullptr || (reinterpret_cast<uintptr_t>(targets) & 3u)))
-        return fail(TP_ERR_INVALID_ARG, "%s: targets is NULL or not 4-byte aligned", fn);
-    TP_TRY(check_elems(fn, N, h));
-    TP_TRY(check_elems(fn, h, v_loc));
-    TP_TRY(check_elems(fn, N, v_loc));
-    return TP_OK;
+tp_status tp_vocab_ce_fwd_workspace_size(int64_t N, int64_t h, int64_t v_loc, size_t* bytes) {
+    const char* fn = "tp_vocab_ce_fwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    TP_TRY(check_ce(fn, N, h, v_loc, 0));
+    *bytes = ce_fwd_need(N, v_loc);
+    return ok();
 }
 
 tp_status tp_vocab_ce_fwd(const void* X, const void* W_i, const int32_t* targets, int64_t vocab_start, int64_t N,
-                          int64_t h, int64_t v_loc, float* m_i, float* s_i, float* zy_i, void* stream) {
+                          int64_t h, int64_t v_loc, float* m_i, float* s_i, float* zy_i, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     const char* fn = "tp_vocab_ce_fwd";
-    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start, targets));
+    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start));
+    TP_TRY(check_targets(fn, N, targets));
     TP_CHECK_TOK_PTR(X, "X");
     TP_CHECK_PTR(W_i, "W_i");
     TP_CHECK_TOK_PTR(m_i, "m_i");
     TP_CHECK_TOK_PTR(s_i, "s_i");
     TP_CHECK_TOK_PTR(zy_i, "zy_i");
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, ce_fwd_need(N, v_loc)));
     if (N == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // records: 2 wave column blocks per kCeTileN-wide tile (launch_gemm runs
-    // EPI_CE_STATS with 256 x 224 tiles of 2 x 2 waves)
-    const int nparts = (int)(2 * ((v_loc + kCeTileN - 1) / kCeTileN));
-    float* rec = nullptr;
-    TP_TRY(workspace(fn, s, (size_t)N * nparts * 3 * sizeof(float), &rec));
+    const int nparts = ce_parts(v_loc);
+    float* rec = static_cast<float*>(workspace);
     GemmArgs a = make_args(X, W_i, rec, (int)N, (int)v_loc, (int)h, (int)h, (int)v_loc, nparts);
     a.tgt = targets;
     a.col0 = (int)vocab_start;
@@ -1001,11 +1195,23 @@ tp_status tp_vocab_ce_combine(const float* m_parts, const float* s_parts, const 
     return ok();
 }
 
+tp_status tp_vocab_ce_bwd_workspace_size(int64_t N, int64_t h, int64_t v_loc, size_t* bytes) {
+    const char* fn = "tp_vocab_ce_bwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    TP_TRY(check_ce(fn, N, h, v_loc, 0));
+    GemmArgs b, c;
+    ce_bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, N, h, v_loc, 0, b, c);
+    *bytes = ce_bwd_need(b, c);
+    return ok();
+}
+
 tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets, int64_t vocab_start,
                           const float* m, const float* S, const float* dloss, int64_t N, int64_t h, int64_t v_loc,
-                          void* dZ, float* dX_part, float* dW_i, int accumulate, void* stream) {
+                          void* dZ, float* dX_part, float* dW_i, int accumulate, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     const char* fn = "tp_vocab_ce_bwd";
-    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start, targets));
+    TP_TRY(check_ce(fn, N, h, v_loc, vocab_start));
+    TP_TRY(check_targets(fn, N, targets));
     TP_CHECK_TOK_PTR(X, "X");
     TP_CHECK_PTR(W_i, "W_i");
     TP_CHECK_TOK_PTR(dZ, "dZ");
@@ -1013,7 +1219,6 @@ tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets
     TP_CHECK_PTR(dW_i, "dW_i");
     if (N > 0 && (!m || !S || !dloss))
         return fail(TP_ERR_INVALID_ARG, "%s: m, S and dloss must not be NULL", fn);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // dZ = (softmax(X W_i) - one-hot) * dloss, the logits recomputed
     GemmArgs a = make_args(X, W_i, dZ, (int)N, (int)v_loc, (int)h, (int)h, (int)v_loc, (int)v_loc);
     a.tgt = targets;
@@ -1021,34 +1226,21 @@ tp_status tp_vocab_ce_bwd(const void* X, const void* W_i, const int32_t* targets
     a.rm = m;
     a.rs = S;
     a.rd = dloss;
-    // dX_part = dZ W_i^T (NT, {U}); dW_i = X^T dZ (TN)
-    GemmArgs b = make_args(dZ, W_i, dX_part, (int)N, (int)h, (int)v_loc, (int)v_loc, (int)v_loc, (int)h);
-    b.accumulate = accumulate ? 1 : 0;
-    GemmArgs c = make_args(X, dZ, dW_i, (int)h, (int)v_loc, (int)N, (int)h, (int)v_loc, (int)v_loc);
-    TP_TRY(reserve(fn, s, {plan_of<false, false, EPI_F32>(b), plan_of<true, true, EPI_F32>(c)}));
+    GemmArgs b, c;
+    ce_bwd_args(X, W_i, dZ, dX_part, dW_i, N, h, v_loc, accumulate, b, c);
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, ce_bwd_need(b, c)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
     TP_TRY((launch_gemm<false, true, EPI_CE_GRAD>(fn, a, s)));
-    TP_TRY((run_gemm<false, false, EPI_F32>(fn, b, s)));
-    TP_TRY((run_gemm<true, true, EPI_F32>(fn, c, s)));
+    TP_TRY((run_gemm<false, false, EPI_F32>(fn, b, workspace, s)));
+    TP_TRY((run_gemm<true, true, EPI_F32>(fn, c, workspace, s)));
     return ok();
-}
-
-static tp_status check_embed(const char* fn, const int32_t* ids, int64_t N, int64_t v_loc, int64_t h,
-                             int64_t vocab_start) {
-    TP_TRY(check_tokens(fn, N));
-    TP_TRY(check_width(fn, "h", h));
-    if (v_loc <= 0 || v_loc > 0x7fffffffLL) return fail(TP_ERR_INVALID_ARG, "%s: v_loc = %lld", fn, (long long)v_loc);
-    if (vocab_start < 0) return fail(TP_ERR_INVALID_ARG, "%s: vocab_start < 0", fn);
-    if (N > 0 && (ids == nullptr || (reinterpret_cast<uintptr_t>(ids) & 3u)))
-        return fail(TP_ERR_INVALID_ARG, "%s: ids is NULL or not 4-byte aligned", fn);
-    TP_TRY(check_elems(fn, v_loc, h));
-    TP_TRY(check_elems(fn, N, h));
-    return TP_OK;
 }
 
 tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_start, int64_t N, int64_t v_loc,
                              int64_t h, void* out, int accumulate, void* stream) {
     const char* fn = "tp_vocab_embed_fwd";
-    TP_TRY(check_embed(fn, ids, N, v_loc, h, vocab_start));
+    TP_TRY(check_embed(fn, N, v_loc, h, vocab_start));
+    TP_TRY(check_ids(fn, N, ids));
     TP_CHECK_PTR(E_i, "E_i");
     TP_CHECK_TOK_PTR(out, "out");
     if (N == 0) return ok();
@@ -1061,18 +1253,26 @@ tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_
     return ok();
 }
 
+tp_status tp_vocab_embed_bwd_workspace_size(int64_t N, int64_t v_loc, int64_t h, size_t* bytes) {
+    const char* fn = "tp_vocab_embed_bwd_workspace_size";
+    TP_QUERY_OUT(bytes);
+    size_t need = 0;
+    TP_TRY(embed_bwd_plan(fn, N, v_loc, h, 0, need));
+    *bytes = need;
+    return ok();
+}
+
 tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_start, int64_t N, int64_t v_loc,
-                             int64_t h, float* dE_i, void* stream) {
+                             int64_t h, float* dE_i, void* workspace, size_t workspace_bytes, void* stream) {
     const char* fn = "tp_vocab_embed_bwd";
-    TP_TRY(check_embed(fn, ids, N, v_loc, h, vocab_start));
-    if (h > kEmbedMaxH) return fail(TP_ERR_UNSUPPORTED, "%s: h = %lld above %d", fn, (long long)h, kEmbedMaxH);
-    if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+    size_t need = 0;
+    TP_TRY(embed_bwd_plan(fn, N, v_loc, h, vocab_start, need));
+    TP_TRY(check_ids(fn, N, ids));
     TP_CHECK_TOK_PTR(dY, "dY");
     TP_CHECK_PTR(dE_i, "dE_i");
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float* ws = nullptr;
-    TP_TRY(workspace(fn, s, (size_t)v_loc * sizeof(uint32_t), &ws));
-    uint32_t* stamp = reinterpret_cast<uint32_t*>(ws);
+    uint32_t* stamp = static_cast<uint32_t*>(workspace);
     static std::atomic<uint32_t> g_stamp{0};
     uint32_t cur = ++g_stamp;
     if (cur == 0) cur = ++g_stamp;  // after 2^32 calls; any value works, see the kernels

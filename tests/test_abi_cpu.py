@@ -108,14 +108,14 @@ def test_vocab_calls_validate_before_launch():
     assert fwd(NULL, NULL, 0, 16, 1000, 100, NULL, 0, NULL) == 3            # h % 64
     bwd = _raw("tp_vocab_embed_bwd")
     odd = ctypes.c_void_p(0x1010)
-    assert bwd(odd, NULL, 0, 16, 1000, 32768, NULL, NULL) == 3              # h above the register tile
+    assert bwd(odd, NULL, 0, 16, 1000, 32768, NULL, NULL, 0, NULL) == 3     # h above the register tile
     ce = _raw("tp_vocab_ce_fwd")
-    assert ce(NULL, NULL, NULL, 0, 16, 8192, 16128, NULL, NULL, NULL, NULL) == 1   # NULL targets
-    assert ce(NULL, NULL, odd, -1, 16, 8192, 16128, NULL, NULL, NULL, NULL) == 1   # vocab_start < 0
+    assert ce(NULL, NULL, NULL, 0, 16, 8192, 16128, NULL, NULL, NULL, NULL, 0, NULL) == 1   # NULL targets
+    assert ce(NULL, NULL, odd, -1, 16, 8192, 16128, NULL, NULL, NULL, NULL, 0, NULL) == 1   # vocab_start < 0
     comb = _raw("tp_vocab_ce_combine")
     assert comb(NULL, NULL, NULL, 0, 16, NULL, NULL, NULL, NULL) == 1               # t = 0
     ch = _raw("tp_row_linear_partial_chunked")
-    assert ch(NULL, NULL, NULL, 16, 1024, 8192, 0, 0, NULL, NULL) == 1             # nchunks = 0
+    assert ch(NULL, NULL, NULL, 16, 1024, 8192, 0, 0, NULL, NULL, 0, NULL) == 1     # nchunks = 0
 
 
 def test_regroup_width_matches_oracle():
@@ -125,21 +125,81 @@ def test_regroup_width_matches_oracle():
 
 def test_gemm_entry_points_validate_before_launch():
     col = _raw("tp_col_linear")
-    assert col(NULL, NULL, NULL, 16, 8192, 1280, 0, NULL, NULL) == 1          # NULL X
-    assert col(NULL, NULL, NULL, 16, 100, 1280, 0, NULL, NULL) == 3           # k % 64
-    assert col(NULL, NULL, NULL, 16, (1 << 20) + 64, 1280, 0, NULL, NULL) == 3  # k above 2^20
+    assert col(NULL, NULL, NULL, 16, 8192, 1280, 0, NULL, NULL, 0, NULL) == 1          # NULL X
+    assert col(NULL, NULL, NULL, 16, 100, 1280, 0, NULL, NULL, 0, NULL) == 3           # k % 64
+    assert col(NULL, NULL, NULL, 16, (1 << 20) + 64, 1280, 0, NULL, NULL, 0, NULL) == 3  # k above 2^20
     assert "too large" in T.tp_last_error()
-    assert col(NULL, NULL, NULL, (1 << 30) + 1, 8192, 1280, 0, NULL, NULL) == 3  # N above 2^30
-    assert col(NULL, NULL, NULL, -1, 8192, 1280, 0, NULL, NULL) == 1          # N < 0
-    assert col(NULL, NULL, NULL, 16, 8192, 1280, 7, NULL, NULL) == 1          # act
+    assert col(NULL, NULL, NULL, (1 << 30) + 1, 8192, 1280, 0, NULL, NULL, 0, NULL) == 3  # N above 2^30
+    assert col(NULL, NULL, NULL, -1, 8192, 1280, 0, NULL, NULL, 0, NULL) == 1          # N < 0
+    assert col(NULL, NULL, NULL, 16, 8192, 1280, 7, NULL, NULL, 0, NULL) == 1          # act
     odd = ctypes.c_void_p(0x1008)
-    assert col(odd, odd, odd, 16, 8192, 1280, 0, NULL, NULL) == 1             # misaligned
+    assert col(odd, odd, odd, 16, 8192, 1280, 0, NULL, NULL, 0, NULL) == 1             # misaligned
     assert "aligned" in T.tp_last_error()
     row = _raw("tp_row_linear_partial")
-    assert row(NULL, NULL, NULL, 16, 1024, 8192, 0, NULL) == 1
+    assert row(NULL, NULL, NULL, 16, 1024, 8192, 0, NULL, 0, NULL) == 1
     fwd = _raw("tp_mlp_shard_fwd")
-    assert fwd(NULL, NULL, NULL, 16, 8192, 3584, 0, NULL, NULL, NULL, 0, NULL) == 1   # act NONE
+    assert fwd(NULL, NULL, NULL, 16, 8192, 3584, 0, NULL, NULL, NULL, 0, NULL, 0, NULL) == 1   # act NONE
     bwd = _raw("tp_mlp_shard_bwd")
     assert bwd(NULL, NULL, NULL, NULL, NULL, NULL, 16, 8192, 3584, 2, NULL, NULL, NULL, NULL, 0,
-               NULL) == 1
+               NULL, 0, NULL) == 1
     assert T.tp_last_error() != ""
+
+
+# Every call that may need scratch memory, with sizes that need some at the
+# Llama-3-70B t = 8 shapes (decode-sized token counts; the narrow attention
+# shards; the cross-entropy records; the embedding stamps) and the arguments
+# of its workspace query.
+WS_CASES = {
+    "tp_col_linear": (16, 8192, 1280, 0),
+    "tp_row_linear_partial": (16, 1024, 8192),
+    "tp_row_linear_partial_chunked": (48, 1024, 8192, 3),
+    "tp_mlp_shard_fwd": (16, 8192, 3584, 2),
+    "tp_row_linear_bwd": (4096, 1024, 8192),
+    "tp_vocab_ce_fwd": (4096, 8192, 16128),
+    "tp_vocab_embed_bwd": (4096, 16128, 8192),
+}
+
+
+@pytest.mark.parametrize("entry", sorted(WS_CASES))
+def test_workspace_queries(entry):
+    n = T.workspace_size(entry, *WS_CASES[entry])
+    assert n > 0 and n % 16 == 0
+    # invalid sizes fail in the query as in the call (a width that is not a
+    # multiple of 64)
+    args = list(WS_CASES[entry])
+    args[2 if entry == "tp_vocab_embed_bwd" else 1] = 100
+    bad = tuple(args)
+    with pytest.raises((ValueError, NotImplementedError)):
+        T.workspace_size(entry, *bad)
+    # NULL output pointer
+    assert getattr(T.load(), entry + "_workspace_size")(*WS_CASES[entry], None) == 1
+
+
+def test_workspace_query_values():
+    # the split-K decode product: ksplit partials of [N, n] f32; the
+    # cross-entropy records: 2 per 224 vocab columns per token, 12 bytes
+    # each; the embedding stamps: 4 bytes per table row
+    n = T.workspace_size("tp_col_linear", 16, 8192, 1280, 0)
+    assert n % (16 * 1280 * 4) == 0 and 2 <= n // (16 * 1280 * 4) <= 64
+    assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 2 * (16128 // 224) * 12
+    assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
+    # products with enough output tiles need none
+    assert T.workspace_size("tp_mlp_shard_fwd", 4096, 8192, 3584, 2) == 0
+    assert T.workspace_size("tp_mlp_shard_bwd", 4096, 8192, 3584, 2) == 0
+    assert T.workspace_size("tp_row_linear_partial", 0, 1024, 8192) == 0
+
+
+def test_too_small_workspace_is_rejected_before_launch():
+    # fake (never dereferenced) aligned device pointers: the call must stop at
+    # the workspace check, before anything is enqueued
+    p = ctypes.c_void_p(0x10000)
+    need = T.workspace_size("tp_col_linear", 16, 8192, 1280, 0)
+    col = _raw("tp_col_linear")
+    assert col(p, p, p, 16, 8192, 1280, 0, NULL, p, need - 16, NULL) == 1
+    assert f"needs {need} bytes" in T.tp_last_error()
+    assert col(p, p, p, 16, 8192, 1280, 0, NULL, NULL, need, NULL) == 1      # NULL workspace
+    assert "NULL" in T.tp_last_error()
+    assert col(p, p, p, 16, 8192, 1280, 0, NULL, ctypes.c_void_p(0x10008), need, NULL) == 1
+    assert "aligned" in T.tp_last_error()
+    emb = _raw("tp_vocab_embed_bwd")
+    assert emb(p, p, 0, 4096, 16128, 8192, p, p, 16128 * 4 - 1, NULL) == 1

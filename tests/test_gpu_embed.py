@@ -43,11 +43,12 @@ def test_embedding_forward_backward(N, V, h, t):
 
 
 def test_table_gradient_calls_in_a_row_and_graph_replays():
-    # Rows used by an earlier call (or marked by bits other calls leave in the
-    # stream's workspace) must come out as exactly what this call's ids give:
-    # successive calls into one buffer with different ids, a split-K product
-    # between them on the same stream, no tokens at all, then graph replays
-    # with the ids rewritten in place between replays.
+    # Rows used by an earlier call (or marked by bits other calls leave in a
+    # shared workspace) must come out as exactly what this call's ids give:
+    # successive calls into one buffer with different ids and one workspace,
+    # a split-K product between them that rewrites that workspace, no tokens
+    # at all, then graph replays (captured on a fresh stream) with the ids
+    # rewritten in place between replays.
     N, V, h = 512, 4096, 512
     v_loc = V // 2
     rng = np.random.default_rng(77)
@@ -56,24 +57,25 @@ def test_table_gradient_calls_in_a_row_and_graph_replays():
     dE = torch.full((v_loc, h), 7.0, dtype=torch.float32, device="cuda:0")
     X = to_dev(synth.draw(rng, (16, 2048)))
     W = to_dev(synth.draw(rng, (2048, 384), fan_in=2048))
+    need = max(T.workspace_size("tp_vocab_embed_bwd", N, v_loc, h),
+               T.workspace_size("tp_col_linear", 16, 2048, 384, 0))
+    assert T.workspace_size("tp_col_linear", 16, 2048, 384, 0) > 0   # the product below is split
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
     for rnd in range(3):
         ids = rng.integers(0, V, size=N).astype(np.int32)
         ids[:8] = rnd * 97 + np.arange(8)            # rows that move from call to call
-        T.tp_vocab_embed_bwd(torch.from_numpy(ids).to("cuda:0"), dYd, 0, v_loc, dE_i=dE)
-        T.tp_col_linear(X, W, "none")                # a split-K product rewrites the workspace
+        T.tp_vocab_embed_bwd(torch.from_numpy(ids).to("cuda:0"), dYd, 0, v_loc, dE_i=dE, workspace=ws)
+        T.tp_col_linear(X, W, "none", workspace=ws)  # a split-K product rewrites the workspace
         torch.cuda.synchronize()
         assert np.array_equal(f64(dE), O.vocab_embed_bwd(ids, dY, 0, v_loc)), rnd
     empty = torch.empty((0,), dtype=torch.int32, device="cuda:0")
-    T.tp_vocab_embed_bwd(empty, dYd[:0], 0, v_loc, dE_i=dE)
+    T.tp_vocab_embed_bwd(empty, dYd[:0], 0, v_loc, dE_i=dE, workspace=ws)
     torch.cuda.synchronize()
     assert not torch.any(dE).item()
 
     idd = torch.from_numpy(rng.integers(0, V, size=N).astype(np.int32)).to("cuda:0")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        T.tp_vocab_embed_bwd(idd, dYd, 0, v_loc, dE_i=dE)   # this stream's workspace exists before capture
-    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         T.tp_vocab_embed_bwd(idd, dYd, 0, v_loc, dE_i=dE)

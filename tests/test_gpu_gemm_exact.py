@@ -99,16 +99,29 @@ def test_split_k_exact(N, k, n):
     assert np.array_equal(f64(P), P0 + O.row_linear_partial(X, W))
 
 
-def test_split_k_workspace_grows_and_shrinks():
-    # one stream, three calls whose split workspaces are small, large, small
-    for i, (N, k, n) in enumerate([(16, 2048, 128), (64, 8192, 256), (8, 1024, 64)]):
+def test_split_k_caller_workspace():
+    # one caller workspace for three calls whose split products need small,
+    # large and small workspaces (the largest size): results exact; a buffer
+    # one byte too small is refused before anything runs
+    shapes = [(16, 2048, 128), (64, 8192, 256), (8, 1024, 64)]
+    need = [T.workspace_size("tp_row_linear_partial", *s) for s in shapes]
+    assert all(x > 0 for x in need) and need[1] > max(need[0], need[2])
+    ws = torch.empty(max(need), dtype=torch.uint8, device="cuda:0")
+    for i, (N, k, n) in enumerate(shapes):
         Xb, X = _ints(30 + i, (N, k))
         Wb, W = _ints(40 + i, (k, n))
         big, P = _canary_f32((N, n))
-        T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb), P=P)
+        T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb), P=P, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(f64(P), O.row_linear_partial(X, W)), (N, k, n)
         assert torch.all(big[N * n:] == SENTINEL)
+    Xb, _ = _ints(33, shapes[1][:2])
+    Wb, _ = _ints(43, shapes[1][1:])
+    P = torch.full(shapes[1][::2], SENTINEL, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError, match="bytes of workspace"):
+        T.tp_row_linear_partial(to_dev(Xb), to_dev(Wb), P=P, workspace=ws[: need[1] - 1])
+    torch.cuda.synchronize()
+    assert torch.all(P == SENTINEL)
 
 
 # (300, 320, 4096): the NT products split K = 4096; (2500, 320, 192): the TN

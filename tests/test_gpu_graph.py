@@ -1,7 +1,9 @@
 """Calls captured into a HIP graph and replayed give the same bits as the same
-calls run eagerly: the split-K decode products (library workspace per stream),
-the MLP forward at decode size and the fused-QKV regroup. Each replay follows
-eager work that rewrites the inputs in place, and every replay is checked."""
+calls run eagerly: the split-K decode products (their workspace allocated by
+the binding inside the capture), the MLP forward at decode size and the
+fused-QKV regroup. Capture works on a fresh stream, with no call before it.
+Each replay follows eager work that rewrites the inputs in place, and every
+replay is checked."""
 import numpy as np
 import pytest
 import torch
@@ -42,11 +44,10 @@ def test_graph_replays_match_eager():
         T.tp_qkv_regroup(W_qkv, 8, 2, 64, 2, 1, W_r=W_r)
 
     outs = (Y, P, Z, Hs, P2, W_r)
-    side = torch.cuda.Stream()
+    assert T.workspace_size("tp_col_linear", N, h, n, 0) > 0        # the decode products are split
+    assert T.workspace_size("tp_row_linear_partial", N, k_o, h) > 0
+    side = torch.cuda.Stream()        # fresh: nothing has run on it
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        calls()  # creates this stream's split-K workspace before capture
-    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         calls()
@@ -75,23 +76,31 @@ def test_graph_replays_match_eager():
     del graph
 
 
-@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # nothing was enqueued, as intended
-def test_capture_before_the_workspace_exists_is_refused():
-    # a stream whose split-K workspace does not exist yet cannot create it
-    # while it is captured: the call reports it and enqueues nothing
+def test_replay_after_larger_eager_calls_on_the_capture_stream():
+    # A captured split product keeps its own workspace: eager calls with
+    # larger split workspaces on the same stream afterwards (which a
+    # per-stream library buffer would have replaced) leave the replays right.
+    dev = "cuda:0"
     N, h, n = 16, 2048, 384
     X = to_dev(_normal(60, (N, h)))
     W = to_dev(_normal(61, (h, n), h))
-    Y = torch.empty((N, n), dtype=torch.bfloat16, device="cuda:0")
+    Y = torch.empty((N, n), dtype=torch.bfloat16, device=dev)
     fresh = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
-    with pytest.raises(ValueError, match="captured"):
-        with torch.cuda.graph(graph, stream=fresh):
-            T.tp_col_linear(X, W, "none", Y=Y)
-    torch.cuda.synchronize()
-    # the same call outside capture works, after which capture does too
-    with torch.cuda.stream(fresh):
+    with torch.cuda.graph(graph, stream=fresh):
         T.tp_col_linear(X, W, "none", Y=Y)
     torch.cuda.synchronize()
+    Xb = to_dev(_normal(62, (64, 8192)))
+    Wb = to_dev(_normal(63, (8192, 1280), 8192))
+    small = T.workspace_size("tp_col_linear", N, h, n, 0)
+    assert T.workspace_size("tp_col_linear", 64, 8192, 1280, 0) > small
     want = O.col_linear(f64(X), f64(W))
-    assert err(f64(Y), want) <= TOL
+    for r in range(3):
+        with torch.cuda.stream(fresh):
+            Yb, _ = T.tp_col_linear(Xb, Wb, "none")     # larger split workspace, eager
+            Y.fill_(0)
+            graph.replay()
+        torch.cuda.synchronize()
+        assert err(f64(Y), want) <= TOL, r
+        assert err(f64(Yb), O.col_linear(f64(Xb), f64(Wb))) <= TOL, r
+    del graph

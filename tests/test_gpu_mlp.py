@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import synth
 import tensor_sharded_matmul_amd as T
-from gpu_util import TOL, err, f64, to_dev
+from gpu_util import TOL, check_errs, err, f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +34,7 @@ def test_mlp_shard_fwd_bwd_parity(act, N, h, F, t):
     errs = {"Z": err(f64(Z), oZ), "H": err(f64(H), oH), "P": err(f64(P), oP),
             "dH": err(f64(dH), g["dH"]), "dX_part": err(f64(dX), g["dX_part"]),
             "dW_in": err(f64(dWi), g["dW_in"]), "dW_out": err(f64(dWo), g["dW_out"])}
-    print(act, N, h, F, t, {k: f"{v:.2e}" for k, v in errs.items()})
-    for k, v in errs.items():
-        assert v <= TOL, (k, v)
+    check_errs(errs, f"{act} N={N} h={h} F={F} t={t}")
 
 
 def test_tiny_gelu_four_shards_sum_to_unsharded():
@@ -68,6 +66,37 @@ def test_accumulate_into_dx_partial():
     torch.cuda.synchronize()
     g = O.mlp_shard_bwd(o["X"], o["W_in"], o["W_out"], synth.bf16_to_f64(dYb), "swiglu")
     assert err(f64(dX), 1.0 + g["dX_part"]) <= TOL
+
+
+@pytest.mark.parametrize("N", [16, 300, 0])
+def test_backward_outputs_skipped_when_not_requested(N):
+    # each subset of {dX_part, dW_in, dW_out}: the requested outputs are the
+    # ones the full call gives (bit for bit: same kernels, same order), the
+    # others are not written
+    d, o = _mlp(50 + N, N, 256, 1024, 4, "swiglu")
+    dYb = synth.mlp_bwd_inputs(51 + N, N, 256)["dY"]
+    X, W_in, W_out, dY = to_dev(d["X"]), to_dev(d["W_in"]), to_dev(d["W_out"]), to_dev(dYb)
+    Z, H, _ = T.tp_mlp_shard_fwd(X, W_in, W_out, "swiglu")
+    full = T.tp_mlp_shard_bwd(X, W_in, W_out, H, Z, dY, "swiglu")
+    torch.cuda.synchronize()
+    g = O.mlp_shard_bwd(o["X"], o["W_in"], o["W_out"], synth.bf16_to_f64(dYb), "swiglu")
+    assert err(f64(full[0]), g["dH"]) <= TOL
+    names = ("dX_part", "dW_in", "dW_out")
+    for mask in range(8):
+        want = tuple(n for i, n in enumerate(names) if mask >> i & 1)
+        outs = {n: torch.full_like(full[1 + i], 7.0) for i, n in enumerate(names)}
+        dH = torch.zeros_like(full[0])
+        res = T.tp_mlp_shard_bwd(X, W_in, W_out, H, Z, dY, "swiglu", dH=dH, want=want,
+                                 **{n: outs[n] for n in want})
+        torch.cuda.synchronize()
+        assert torch.equal(dH.view(torch.int16), full[0].view(torch.int16)), mask
+        for i, n in enumerate(names):
+            if n in want:
+                assert res[1 + i] is outs[n]
+                assert torch.equal(outs[n], full[1 + i]), (mask, n)
+            else:
+                assert res[1 + i] is None
+                assert bool(torch.all(outs[n] == 7.0)), (mask, n)
 
 
 @pytest.mark.parametrize("N", [16, 300])

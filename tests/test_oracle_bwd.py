@@ -97,3 +97,24 @@ def test_sampled_forms_match_full(act):
     sel = np.concatenate([cols, f + cols]) if act == "swiglu" else cols
     assert np.allclose(bc["dW_in_cols"], g["dW_in"][:, sel])
     assert np.allclose(bc["dW_out_rows"], g["dW_out"][cols])
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_bwd_from_saved_tensors_is_the_recomputing_bwd(act):
+    # mlp_shard_bwd recomputes H, Z; mlp_shard_bwd_saved takes the forward's:
+    # the same gradients (and a planted swap of Z for H fails)
+    rng = np.random.default_rng(11)
+    N, h, f = 5, 6, 4
+    n_w = 2 * f if act == "swiglu" else f
+    X = rng.standard_normal((N, h))
+    W_in = rng.standard_normal((h, n_w))
+    W_out = rng.standard_normal((f, h))
+    dY = rng.standard_normal((N, h))
+    Z, H, _ = O.mlp_shard_fwd(X, W_in, W_out, act)
+    g = O.mlp_shard_bwd(X, W_in, W_out, dY, act)
+    s = O.mlp_shard_bwd_saved(X, W_in, W_out, H, Z, dY, act)
+    for k in ("dZ", "dH", "dX_part", "dW_in", "dW_out"):
+        assert np.array_equal(g[k], s[k]), k
+    if act == "gelu":
+        wrong = O.mlp_shard_bwd_saved(X, W_in, W_out, Z, Z, dY, act)
+        assert not np.allclose(wrong["dX_part"], g["dX_part"])

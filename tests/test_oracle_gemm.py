@@ -142,3 +142,21 @@ def test_swiglu_shard_layout_is_gate_then_up():
     Zg, Hg = O.col_linear_act(X, W, "gelu")
     assert np.allclose(Hg, O.matmul_loops(X, W), rtol=1e-13, atol=1e-13)
     assert Zg.shape == (5, 8) and Z.shape == (5, 4)
+
+
+def test_rel_err_is_max_abs_diff_over_max_abs_reference():
+    # the parity metric, max|got - want| / max|want|, on values where the
+    # plausible slips (mean instead of max, the denominator taken from
+    # `got`, a signed instead of absolute difference) give other numbers
+    got = np.array([[1.0, 2.0], [3.0, -4.0]])
+    want = np.array([[1.0, 2.5], [5.0, -4.0]])
+    assert O.rel_err(got, want) == pytest.approx(2.0 / 5.0)
+    assert O.rel_err(want, got) == pytest.approx(2.0 / 4.0)          # not symmetric
+    assert O.rel_err(-got, -want) == pytest.approx(0.4)
+    assert np.mean(np.abs(got - want)) / np.mean(np.abs(want)) != pytest.approx(0.4)
+    assert O.rel_err(np.array([1.0, 3.0]), np.array([2.0, 1.0])) == pytest.approx(2.0 / 2.0)
+    # a reference of zeros: the plain maximum error; empty: 0
+    assert O.rel_err(np.array([0.5, -1.5]), np.zeros(2)) == pytest.approx(1.5)
+    assert O.rel_err(np.zeros(0), np.zeros(0)) == 0.0
+    # NaN in the result is never within any tolerance
+    assert not O.rel_err(np.array([np.nan, 1.0]), np.array([1.0, 1.0])) <= 1.0
