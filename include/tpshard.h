@@ -118,6 +118,22 @@ tp_status tp_col_linear(const void* X, const void* W, void* Y,
                         void* stream);
 
 /*
+ * tp_col_linear for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments except the workspace, the same kernels and results. A split
+ * product's partials go to a device array inside the library (16 MiB, one
+ * per device, held until the process ends) instead of a workspace; a call
+ * whose split needs more (tp_col_linear_workspace_size > 16 MiB, e.g. wide
+ * products at more than 64 tokens) returns TP_ERR_UNSUPPORTED before any
+ * launch. Nothing is allocated. Every call on one device shares that array:
+ * calls that may overlap on a device (different streams, or graphs replayed
+ * concurrently) race on it and must be serialised by the caller.
+ */
+tp_status tp_col_linear_noalloc(const void* X, const void* W, void* Y,
+                                int64_t N, int64_t k, int64_t n_out, int act,
+                                void* H_save, void* stream);
+
+/*
  * Row-parallel linear, partial sum ([TPSP] "矩阵乘法的两种切法", second
  * identity; [REVISIT] Row-wise TP). The rank holds the input slice
  * Z_i[N, k_loc] and the weight row block W_i[k_loc, n]; Z_i W_i is a

@@ -23,7 +23,7 @@ __all__ = [
     "tp_col_linear_bwd", "tp_row_linear_bwd", "tp_qkv_regroup", "tp_shard_shape",
     "tp_row_linear_partial_chunked", "tp_kv_grad_accumulate", "tp_vocab_ce_fwd",
     "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_embed_fwd", "tp_vocab_embed_bwd",
-    "workspace_size", "regroup_width", "ACT", "TPError",
+    "tp_col_linear_noalloc", "workspace_size", "regroup_width", "ACT", "TPError",
 ]
 
 ACT = {"none": 0, "gelu": 1, "swiglu": 2}
@@ -59,6 +59,7 @@ def load():
         "tp_last_error": ([], ctypes.c_char_p),
         "tp_col_linear_workspace_size": ([i64, i64, i64, i, psz], i),
         "tp_col_linear": ([vp, vp, vp, i64, i64, i64, i, vp, vp, sz, vp], i),
+        "tp_col_linear_noalloc": ([vp, vp, vp, i64, i64, i64, i, vp, vp], i),
         "tp_row_linear_partial_workspace_size": ([i64, i64, i64, psz], i),
         "tp_row_linear_partial": ([vp, vp, vp, i64, i64, i64, i, vp, sz, vp], i),
         "tp_row_linear_partial_chunked_workspace_size": ([i64, i64, i64, i32, psz], i),
@@ -190,6 +191,23 @@ def tp_col_linear(X, W, act="none", Y=None, H_save=None, want_h=False, workspace
     wp, wn, _keep = _workspace("tp_col_linear", (N, k, n_out, a), X, stream, workspace)
     _check(lib.tp_col_linear(_ptr(X), _ptr(W), _ptr(Y), N, k, n_out, a, _ptr(H_save), wp, wn,
                              _stream(stream)))
+    return Y, H_save
+
+
+def tp_col_linear_noalloc(X, W, Y, act="none", H_save=None, stream=None):
+    """tp_col_linear with the library's device scratch instead of a workspace
+    (the C call allocates nothing; Y and H_save must be given)."""
+    lib = load()
+    a = ACT[act]
+    N, k = X.shape
+    n_w = W.shape[1]
+    n_out = n_w // 2 if act == "swiglu" else n_w
+    _dev(X, "X", _bf16, (N, k))
+    _dev(W, "W", _bf16, (k, n_w))
+    _dev(Y, "Y", _bf16, (N, n_out))
+    if H_save is not None:
+        _dev(H_save, "H_save", _bf16, (N, n_w))
+    _check(lib.tp_col_linear_noalloc(_ptr(X), _ptr(W), _ptr(Y), N, k, n_out, a, _ptr(H_save), _stream(stream)))
     return Y, H_save
 
 

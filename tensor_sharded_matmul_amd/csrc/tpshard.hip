@@ -611,6 +611,39 @@ __global__ void __launch_bounds__(256) qkv_regroup_kernel(const uint16_t* __rest
 }  // namespace tps
 
 // ---------------------------------------------------------------------------
+// Scratch of tp_col_linear_noalloc: device memory that is part of the code
+// object, so that callers that cannot allocate (graph capture of a serving
+// loop, harnesses that forbid allocation) can run split products. Each device
+// holds its own copy at its own address, looked up once per device; in host
+// code the array's name is not a device address.
+// ---------------------------------------------------------------------------
+namespace tps {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static tp_status scratch_address(const char* fn, void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(TP_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(TP_ERR_HIP, "%s: address of the device scratch: %s", fn, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return TP_OK;
+}
+
+}  // namespace tps
+
+// ---------------------------------------------------------------------------
 // Each entry point that runs GEMMs first validates its sizes and describes
 // its products (pointers may be NULL here: the host-only workspace queries
 // run the same code), giving the workspace bytes its split products need.
@@ -881,6 +914,25 @@ tp_status tp_col_linear(const void* X, const void* W, void* Y, int64_t N, int64_
     TP_CHECK_OPT_PTR(H_save, "H_save");
     TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     TP_TRY(col_linear_run(fn, a, act, workspace, static_cast<hipStream_t>(stream)));
+    return ok();
+}
+
+tp_status tp_col_linear_noalloc(const void* X, const void* W, void* Y, int64_t N, int64_t k, int64_t n_out,
+                                int act, void* H_save, void* stream) {
+    const char* fn = "tp_col_linear_noalloc";
+    GemmArgs a;
+    size_t need = 0;
+    TP_TRY(col_linear_plan(fn, X, W, Y, N, k, n_out, act, H_save, a, need));
+    TP_CHECK_TOK_PTR(X, "X");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_TOK_PTR(Y, "Y");
+    TP_CHECK_OPT_PTR(H_save, "H_save");
+    if (need > kScratchBytes)
+        return fail(TP_ERR_UNSUPPORTED, "%s: the product needs %zu bytes of scratch, above the library's %zu",
+                    fn, need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) TP_TRY(scratch_address(fn, &ws));
+    TP_TRY(col_linear_run(fn, a, act, ws, static_cast<hipStream_t>(stream)));
     return ok();
 }
 

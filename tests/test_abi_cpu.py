@@ -203,3 +203,14 @@ def test_too_small_workspace_is_rejected_before_launch():
     assert "aligned" in T.tp_last_error()
     emb = _raw("tp_vocab_embed_bwd")
     assert emb(p, p, 0, 4096, 16128, 8192, p, p, 16128 * 4 - 1, NULL) == 1
+
+
+def test_noalloc_entry_point_validates_before_launch():
+    f = _raw("tp_col_linear_noalloc")
+    p = ctypes.c_void_p(0x10000)
+    assert f(NULL, NULL, NULL, 16, 8192, 1280, 0, NULL, NULL) == 1          # NULL X
+    assert f(p, p, p, 16, 100, 1280, 0, NULL, NULL) == 3                    # k % 64
+    # the QKV product at 4096 tokens splits into more than the 16 MiB scratch
+    assert T.workspace_size("tp_col_linear", 4096, 8192, 1280, 0) > 16 << 20
+    assert f(p, p, p, 4096, 8192, 1280, 0, NULL, NULL) == 3
+    assert "scratch" in T.tp_last_error()
