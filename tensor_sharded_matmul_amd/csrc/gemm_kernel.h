@@ -583,24 +583,38 @@ __device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const Gem
         epilogue_ce_grad<MI, NI>(acc, args, mb, nb);
         return;
     }
+    if constexpr (EPI == EPI_F32) {
+        // one pass per mode, rows one at a time: the accumulators move to
+        // VGPRs a row at a time (a test inside the row loop made the
+        // compiler copy them all first)
+        auto rows = [&](auto accc) {
+            constexpr bool ACC = decltype(accc)::value;
+            static_for<0, MI>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const int m = mb + i * 16;
+                if (m < args.M) {
+                    f32x4_t* row =
+                        reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb);
+                    static_for<0, NI>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        if (nb + j * 16 < args.N) {
+                            if constexpr (ACC) row[j * 4] = acc[i][j] + row[j * 4];
+                            else row[j * 4] = acc[i][j];
+                        }
+                    });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        if (args.accumulate) rows(std::true_type{});
+        else rows(std::false_type{});
+        return;
+    }
     static_for<0, MI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const int m = mb + i * 16;
         if (m < args.M) {
-            if constexpr (EPI == EPI_F32) {
-                f32x4_t* row = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb);
-                if (args.accumulate) {
-                    static_for<0, NI>([&](auto jc) {
-                        constexpr int j = decltype(jc)::value;
-                        if (nb + j * 16 < args.N) row[j * 4] = acc[i][j] + row[j * 4];
-                    });
-                } else {
-                    static_for<0, NI>([&](auto jc) {
-                        constexpr int j = decltype(jc)::value;
-                        if (nb + j * 16 < args.N) row[j * 4] = acc[i][j];
-                    });
-                }
-            } else if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU) {
+            if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU) {
                 uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
                 static_for<0, NI>([&](auto jc) {
                     constexpr int j = decltype(jc)::value;
@@ -640,6 +654,31 @@ __device__ __forceinline__ void epilogue(const f32x4_t (&acc)[MI][NI], const Gem
                     }
                 });
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// fp32 store of the accumulators straight from their registers (ping-pong
+// kernels, which keep only half of the VGPRs: a plain C++ store makes the
+// compiler copy every accumulator to VGPRs first). Overwrites C; the
+// launcher runs products that add into C on the other kernels.
+__device__ __forceinline__ void store_f32x4_acc(float* p, const f32x4_t& v) {
+    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "a"(v) : "memory");
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_f32_store_acc(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,
+                                                       int nb) {
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int m = mb + i * 16;
+        if (m < args.M) {
+            float* row = reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb;
+            static_for<0, NI>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (nb + j * 16 < args.N) store_f32x4_acc(row + j * 16, acc[i][j]);
+            });
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -715,11 +754,14 @@ __device__ __forceinline__ void epilogue_swx_up(const f32x4_t (&acc)[MI][NI], co
 // load unit returns data). An MN-contiguous operand has whole lines at any
 // depth and uses 32-row stages, so that more of them fit in flight.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int TM_, int TN_, int BKA_, int SA_, int BKB_, int SB_, int WAVES_M_, int WAVES_N_>
+//   PP        ping-pong schedule (8 waves; see the kernel's k-loop)
+template <int BM_, int BN_, int TM_, int TN_, int BKA_, int SA_, int BKB_, int SB_, int WAVES_M_, int WAVES_N_,
+          bool PP_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, TM = TM_, TN = TN_;
     static constexpr int BKA = BKA_, SA = SA_, BKB = BKB_, SB = SB_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr bool PP = PP_;
 };
 
 // ---------------------------------------------------------------------------
@@ -833,23 +875,27 @@ gemm_kernel(const GemmArgs args) {
                            (A_T ? 0u : (uint64_t)m0 * (uint64_t)args.lda * 2u);
     const uint64_t b_org = (uint64_t)k0 * (B_KN ? (uint64_t)args.ldb : 1u) * 2u +
                            (B_KN ? 0u : (uint64_t)n0 * (uint64_t)args.ldb * 2u);
-    using ADma = typename std::conditional<A_T, MNTileDma<BM, BKA, NWAVES>, KTileDma<BM, BKA, NWAVES>>::type;
-    using BDma = typename std::conditional<B_KN, MNTileDma<BN, BKB, NWAVES>, KTileDma<BN, BKB, NWAVES>>::type;
+    // every wave issues its share of each stage's LDS-DMA loads
+    constexpr bool PP = CF::PP;
+    constexpr int NWD = NWAVES;
+    const int dw = wave;
+    using ADma = typename std::conditional<A_T, MNTileDma<BM, BKA, NWD>, KTileDma<BM, BKA, NWD>>::type;
+    using BDma = typename std::conditional<B_KN, MNTileDma<BN, BKB, NWD>, KTileDma<BN, BKB, NWD>>::type;
     ADma da;
     BDma db;
     if constexpr (A_T) {
-        da.init(wave, lane, args.lda, IdentityCols{m0, args.M});
+        da.init(dw, lane, args.lda, IdentityCols{m0, args.M});
     } else {
-        da.init(wave, lane, 0, args.lda);
+        da.init(dw, lane, 0, args.lda);
     }
     if constexpr (B_KN) {
         if constexpr (GATEUP) {
-            db.init(wave, lane, args.ldb, SwigluCols<BN / 2>{n0, args.f});
+            db.init(dw, lane, args.ldb, SwigluCols<BN / 2>{n0, args.f});
         } else {
-            db.init(wave, lane, args.ldb, IdentityCols{n0, args.N});
+            db.init(dw, lane, args.ldb, IdentityCols{n0, args.N});
         }
     } else {
-        db.init(wave, lane, 0, args.ldb);
+        db.init(dw, lane, 0, args.ldb);
     }
     // An MN-contiguous operand of a split-K product is range-checked up to
     // the end of this split's K rows: the ring's loads past the chunk (issued
@@ -869,10 +915,10 @@ gemm_kernel(const GemmArgs args) {
     // load d of this wave's share of a stage of operand A / B: LDS buffer at
     // byte offset `buf` of the ring, the stage's descriptor and k offset
     auto issue_a = [&](auto dc, uint32_t buf, i32x4_t rs, uint32_t ko) {
-        da.issue_one(decltype(dc)::value, rs, ldsA + buf, wave, ko);
+        da.issue_one(decltype(dc)::value, rs, ldsA + buf, dw, ko);
     };
     auto issue_b = [&](auto dc, uint32_t buf, i32x4_t rs, uint32_t ko) {
-        db.issue_one(decltype(dc)::value, rs, ldsB + buf, wave, ko);
+        db.issue_one(decltype(dc)::value, rs, ldsB + buf, dw, ko);
     };
 
     // --- fragment addresses in buffer 0 of each ring ---
@@ -950,7 +996,7 @@ gemm_kernel(const GemmArgs args) {
     };
     // (decode tiles, at most 32 token rows, stream the weight and are bound
     // by HBM, not by the MFMA issue; they may load more often than they MFMA)
-    static_assert(NMFMA >= LA + LB || TM <= 32, "fewer MFMAs than loads per sub-step");
+    static_assert(PP || NMFMA >= LA + LB || TM <= 32, "fewer MFMAs than loads per sub-step");
 
     // the waits the model derives are the same for every sub-step of a parity
     static_assert(ring.wait_count(0) == ring.wait_count(2) && ring.wait_count(2) == ring.wait_count(4) &&
@@ -1025,62 +1071,238 @@ gemm_kernel(const GemmArgs args) {
         if constexpr (IB) b_wr = wrap_b(b_wr);
     };
 
-    if (U > 0) {  // K = 0 (no tokens in a weight gradient): C = 0
-        // prologue: the stages issued "before sub-step 0", in the model's
-        // order, then sub-step 0's fragments go to registers
-        // (keys run from the earlier of the two stage 0s up to -1)
-        constexpr int kmin = ring.key(0, 0) < ring.key(1, 0) ? ring.key(0, 0) : ring.key(1, 0);
-        static_for<0, -kmin>([&](auto kc) {
-            constexpr int key = decltype(kc)::value + kmin;
+    if constexpr (PP) {
+        // Ping-pong: the two waves of each SIMD (wave w and w + 4: groups 0
+        // and 1) take turns, phase by phase, between a run of MFMAs and the
+        // memory work of their next sub-step (fragment reads and their share
+        // of the LDS-DMA loads), so the matrix pipe of a SIMD is fed by one
+        // wave while the other's loads and reads are in flight. Per sub-step
+        // u, with a barrier after each phase:
+        //   phase 2u:     group 0 MFMAs of u  | group 1 reads u, issues the
+        //                                       stages due at u - 1
+        //   phase 2u + 1: group 1 MFMAs of u  | group 0 reads u + 1, issues
+        //                                       the stages due at u
+        // (a stage is due when the buffer it refills has been read by both
+        // groups). Each wave issues its share of every stage (the ring model
+        // of the interleaved schedule, with 8 waves' shares), so the loads
+        // of a sub-step are spread over both phases; a group waits for a
+        // stage at the end of the phase before the first reads of it, and
+        // drains its LDS reads before the barrier that ends its memory
+        // phase. Fragments are single-buffered: a wave's reads follow its
+        // own MFMAs.
+        static_assert(NWAVES == 8, "ping-pong: two groups of four waves, one of each per SIMD");
+        const bool g0 = wave < NWAVES / 2;
+        if (U > 0) {
+            constexpr int kmin = ring.key(0, 0) < ring.key(1, 0) ? ring.key(0, 0) : ring.key(1, 0);
             {
-                constexpr int o = ((key % 2) + 2) % 2;      // operand of this key
-                constexpr int t = (key - o) / 2;            // its sub-step
-                // stage st with t_o(st) == t, if any and if st >= 0
-                constexpr int pp = o == 0 ? PA : PB, SS = o == 0 ? SA : SB;
-                if constexpr ((t + 1) % pp == 0 && (t + 1) / pp + SS - 1 >= 0) {
-                    constexpr int st = (t + 1) / pp + SS - 1;
-                    if constexpr (o == 0) {
-                        static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), ca.rs, ca.ko); });
+                static_for<0, -kmin>([&](auto kc) {
+                    constexpr int key = decltype(kc)::value + kmin;
+                    constexpr int o = ((key % 2) + 2) % 2;
+                    constexpr int t = (key - o) / 2;
+                    constexpr int pp = o == 0 ? PA : PB, SS = o == 0 ? SA : SB;
+                    if constexpr ((t + 1) % pp == 0 && (t + 1) / pp + SS - 1 >= 0) {
+                        constexpr int st = (t + 1) / pp + SS - 1;
+                        if constexpr (o == 0) {
+                            static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), ca.rs, ca.ko); });
+                            ca.next();
+                        } else {
+                            static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), cb.rs, cb.ko); });
+                            cb.next();
+                        }
+                    }
+                });
+            }
+            constexpr int W0 = [] {
+                constexpr RingModel rm{PA, SA, LA, PB, SB, LB};
+                const int kmax = rm.key(0, 0) > rm.key(1, 0) ? rm.key(0, 0) : rm.key(1, 0);
+                int x = 0;
+                for (int st = 0; rm.t_of(0, st) < 0; ++st)
+                    if (rm.key(0, st) > kmax) x += LA;
+                for (int st = 0; rm.t_of(1, st) < 0; ++st)
+                    if (rm.key(1, st) > kmax) x += LB;
+                return x;
+            }();
+            wait_vmcnt_barrier<W0>();
+            Frags fr;
+            auto read_all = [&](auto hac, auto hbc) {
+                static_for<0, NFR>([&](auto rc) { read_one(fr, rc, a_rd, b_rd, hac, hbc); });
+            };
+            auto mfma_run = [&]() {
+                __builtin_amdgcn_s_setprio(1);
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, NMFMA>([&](auto mc) {
+                    mfma_one(fr, mc);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // end of a memory phase: this wave's reads are in registers (and
+            // its last reads of a buffer are done) before the barrier
+            auto reads_done_barrier = [&]() {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                asm volatile("s_barrier" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // after a barrier, before reads overwrite fragments that MFMAs of
+            // the previous phase took as operands
+            auto operand_gap = [&]() {
+                asm volatile("s_nop 7" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            if (g0) read_all(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_nop 4" ::: "memory");  // VALU-zeroed accumulators before the first MFMA
+            __builtin_amdgcn_sched_barrier(0);
+            auto g0_step = [&](auto parc) {
+                constexpr int PAR = decltype(parc)::value;
+                constexpr bool IA = ring.issues(0, PAR), IB = ring.issues(1, PAR);
+                mfma_run();
+                if constexpr (IA || IB) {
+                    wait_vmcnt_barrier<ring.wait_count(PAR)>();
+                } else {
+                    asm volatile("s_barrier" ::: "memory");
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                operand_gap();
+                if constexpr (IA) a_rd = wrap_a(a_rd);
+                if constexpr (IB) b_rd = wrap_b(b_rd);
+                read_all(std::integral_constant<int, (PAR + 1) % PA>{}, std::integral_constant<int, (PAR + 1) % PB>{});
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (IA) {
+                    static_for<0, LA>([&](auto dc) {
+                        issue_a(dc, a_wr, ca.rs, ca.ko);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    ca.next();
+                    a_wr = wrap_a(a_wr);
+                }
+                if constexpr (IB) {
+                    static_for<0, LB>([&](auto dc) {
+                        issue_b(dc, b_wr, cb.rs, cb.ko);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    cb.next();
+                    b_wr = wrap_b(b_wr);
+                }
+                reads_done_barrier();
+            };
+            auto g1_step = [&](auto parc, bool first) {
+                constexpr int PAR = decltype(parc)::value;
+                // stages due at u - 1 (none before sub-step 1: the
+                // prologue issued those)
+                constexpr bool JA = PAR % PA == 0, JB = PAR % PB == 0;
+                constexpr bool IA = ring.issues(0, PAR), IB = ring.issues(1, PAR);
+                operand_gap();
+                read_all(std::integral_constant<int, PAR % PA>{}, std::integral_constant<int, PAR % PB>{});
+                if constexpr (IA) a_rd = wrap_a(a_rd);
+                if constexpr (IB) b_rd = wrap_b(b_rd);
+                __builtin_amdgcn_sched_barrier(0);
+                if (!first) {
+                    if constexpr (JA) {
+                        static_for<0, LA>([&](auto dc) {
+                            issue_a(dc, a_wr, ca.rs, ca.ko);
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
                         ca.next();
-                    } else {
-                        static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), cb.rs, cb.ko); });
+                        a_wr = wrap_a(a_wr);
+                    }
+                    if constexpr (JB) {
+                        static_for<0, LB>([&](auto dc) {
+                            issue_b(dc, b_wr, cb.rs, cb.ko);
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
                         cb.next();
+                        b_wr = wrap_b(b_wr);
                     }
                 }
+                // group 0 reads stage (u + 1) / p next: this wave's share of
+                // it has landed (and its reads are in registers)
+                if constexpr (IA || IB) {
+                    wait_vmcnt_barrier<ring.wait_count(PAR)>();
+                } else {
+                    reads_done_barrier();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_run();
+                asm volatile("s_barrier" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            if (g0) {
+                for (int u = 0; u < U; u += 2) {
+                    g0_step(std::integral_constant<int, 0>{});
+                    g0_step(std::integral_constant<int, 1>{});
+                }
+            } else {
+                for (int u = 0; u < U; u += 2) {
+                    g1_step(std::integral_constant<int, 0>{}, u == 0);
+                    g1_step(std::integral_constant<int, 1>{}, false);
+                }
             }
-        });
-        // stage 0 of both rings landed: every load issued after the later of
-        // the two may stay outstanding
-        constexpr int W0 = [] {
-            constexpr RingModel rm{PA, SA, LA, PB, SB, LB};
-            const int kmax = rm.key(0, 0) > rm.key(1, 0) ? rm.key(0, 0) : rm.key(1, 0);
-            int x = 0;
-            for (int st = 0; rm.t_of(0, st) < 0; ++st)
-                if (rm.key(0, st) > kmax) x += LA;
-            for (int st = 0; rm.t_of(1, st) < 0; ++st)
-                if (rm.key(1, st) > kmax) x += LB;
-            return x;
-        }();
-        wait_vmcnt_barrier<W0>();
-        Frags f0, f1;
-        static_for<0, NFR>([&](auto rc) {
-            read_one(f0, rc, 0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-        });
-        // the accumulators were zeroed by VALU writes, which the first MFMA
-        // (inline asm, invisible to the hazard checks) must not overtake
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 4" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        for (int u = 0; u < U; u += 2) {
-            substep(std::integral_constant<int, 0>{}, f0, f1);
-            substep(std::integral_constant<int, 1>{}, f1, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // MFMA results are read by the epilogue only after the longest
-        // MFMA-write -> read wait (the checks do not see the asm MFMAs), and
-        // after every LDS-DMA load has retired
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        if (U > 0) {  // K = 0 (no tokens in a weight gradient): C = 0
+            // prologue: the stages issued "before sub-step 0", in the model's
+            // order, then sub-step 0's fragments go to registers
+            // (keys run from the earlier of the two stage 0s up to -1)
+            constexpr int kmin = ring.key(0, 0) < ring.key(1, 0) ? ring.key(0, 0) : ring.key(1, 0);
+            static_for<0, -kmin>([&](auto kc) {
+                constexpr int key = decltype(kc)::value + kmin;
+                {
+                    constexpr int o = ((key % 2) + 2) % 2;      // operand of this key
+                    constexpr int t = (key - o) / 2;            // its sub-step
+                    // stage st with t_o(st) == t, if any and if st >= 0
+                    constexpr int pp = o == 0 ? PA : PB, SS = o == 0 ? SA : SB;
+                    if constexpr ((t + 1) % pp == 0 && (t + 1) / pp + SS - 1 >= 0) {
+                        constexpr int st = (t + 1) / pp + SS - 1;
+                        if constexpr (o == 0) {
+                            static_for<0, LA>([&](auto dc) { issue_a(dc, (uint32_t)(st * A_STAGE), ca.rs, ca.ko); });
+                            ca.next();
+                        } else {
+                            static_for<0, LB>([&](auto dc) { issue_b(dc, (uint32_t)(st * B_STAGE), cb.rs, cb.ko); });
+                            cb.next();
+                        }
+                    }
+                }
+            });
+            // stage 0 of both rings landed: every load issued after the later of
+            // the two may stay outstanding
+            constexpr int W0 = [] {
+                constexpr RingModel rm{PA, SA, LA, PB, SB, LB};
+                const int kmax = rm.key(0, 0) > rm.key(1, 0) ? rm.key(0, 0) : rm.key(1, 0);
+                int x = 0;
+                for (int st = 0; rm.t_of(0, st) < 0; ++st)
+                    if (rm.key(0, st) > kmax) x += LA;
+                for (int st = 0; rm.t_of(1, st) < 0; ++st)
+                    if (rm.key(1, st) > kmax) x += LB;
+                return x;
+            }();
+            wait_vmcnt_barrier<W0>();
+            Frags f0, f1;
+            static_for<0, NFR>([&](auto rc) {
+                read_one(f0, rc, 0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+            });
+            // the accumulators were zeroed by VALU writes, which the first MFMA
+            // (inline asm, invisible to the hazard checks) must not overtake
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 4" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < U; u += 2) {
+                substep(std::integral_constant<int, 0>{}, f0, f1);
+                substep(std::integral_constant<int, 1>{}, f1, f0);
+            }
+            // MFMA results are read by the epilogue only after the longest
+            // MFMA-write -> read wait (the checks do not see the asm MFMAs), and
+            // after every LDS-DMA load has retired
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     const int lr = lane & 15, lq = lane >> 4;
@@ -1105,13 +1327,15 @@ gemm_kernel(const GemmArgs args) {
         __syncthreads();
         if (wn == 0) epilogue_swx_gate<MI, NI>(acc, args, mb, nb, xch);
         else epilogue_swx_up<MI, NI>(acc, args, mb, nb);
-    } else if constexpr (EPI == EPI_F32) {  // split-K partials are plain fp32 stores
+    } else if constexpr (EPI == EPI_F32 && !PP) {  // split-K partials are plain fp32 stores
         GemmArgs part = args;
         if (args.ksplit > 1) {
             part.C = reinterpret_cast<float*>(args.C) + (size_t)split * args.M * args.ldc;
             part.accumulate = 0;
         }
         epilogue<MI, NI, EPI_F32>(acc, part, mb, nb);
+    } else if constexpr (EPI == EPI_F32) {  // ping-pong: one K split, C overwritten
+        epilogue_f32_store_acc<MI, NI>(acc, args, mb, nb);
     } else {
         epilogue<MI, NI, EPI>(acc, args, mb, nb);
     }

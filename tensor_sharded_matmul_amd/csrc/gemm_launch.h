@@ -10,6 +10,12 @@
 #include "gemm_kernel.h"
 
 namespace tps {
+// Products of one K split whose operand windows are below 2^31 bytes run the
+// ping-pong schedule (8 waves, the two of a SIMD alternating between MFMAs
+// and memory work) on the large tiles.
+#ifndef TPS_PP
+#define TPS_PP 1
+#endif
 
 // Records a formatted message for tp_last_error and returns st.
 tp_status fail(tp_status st, const char* fmt, ...);
@@ -19,6 +25,29 @@ tp_status fail(tp_status st, const char* fmt, ...);
 // descriptor along K (the WIDE variant).
 inline bool mn_window_wide(bool mn, int64_t K, int64_t ld) {
     return mn && (K + 512) * ld * 2 >= ((int64_t)1 << 31);
+}
+
+template <class CF, bool A_T, bool B_KN, int EPI>
+inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s);
+
+// The ping-pong configuration PPC when the product allows it (one K split,
+// no WIDE window, no fp32 accumulation into C), else the interleaved one CF.
+template <class CF, class PPC, bool A_T, bool B_KN, int EPI>
+inline tp_status launch_pp_or(const char* fn, const GemmArgs& a, hipStream_t s) {
+    // forward (NN) products only: on the backward layouts the ping-pong
+    // kernels measured 2-5 % slower (NT: the 160 KB ring leaves group 1's
+    // share of a stage one sub-step to land; TN: lower MFMA busy at the
+    // same clock)
+    if constexpr (TPS_PP != 0 && !A_T && B_KN) {
+        bool wide = false;
+        if constexpr (A_T || B_KN)
+            wide = mn_window_wide(A_T, a.K, a.lda) || mn_window_wide(B_KN, a.K, a.ldb);
+        // (an fp32 product that adds into C runs the interleaved kernel: the
+        // ping-pong one stores its accumulators as they are)
+        const bool adds = EPI == EPI_F32 && a.accumulate;
+        if (a.ksplit == 1 && !wide && !adds) return launch_cfg<PPC, A_T, B_KN, EPI>(fn, a, s);
+    }
+    return launch_cfg<CF, A_T, B_KN, EPI>(fn, a, s);
 }
 
 template <class CF, bool A_T, bool B_KN, int EPI>
@@ -32,7 +61,8 @@ inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
     if constexpr (A_T || B_KN)
         wide = mn_window_wide(A_T, a.K, a.lda) || mn_window_wide(B_KN, a.K, a.ldb);
     if (wide) {
-        if constexpr (A_T || B_KN) hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI, true>), grid, block, 0, s, a);
+        if constexpr ((A_T || B_KN) && !CF::PP)
+            hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI, true>), grid, block, 0, s, a);
     } else {
         hipLaunchKernelGGL((gemm_kernel<CF, A_T, B_KN, EPI, false>), grid, block, 0, s, a);
     }
@@ -88,6 +118,33 @@ template <bool A_T, bool B_KN, int BM, int BN, int TM, int TN, int WVM, int WVN>
 using CfgOf = Cfg<BM, BN, TM, TN, Rings<A_T, B_KN>::BKA, Rings<A_T, B_KN>::SA, Rings<A_T, B_KN>::BKB,
                   Rings<A_T, B_KN>::SB, WVM, WVN>;
 
+// Rings of the ping-pong schedule. The share of a stage that group 1 loads
+// is issued one phase after group 0's, so a ring of two 64-row stages leaves
+// it one sub-step to land; NN and TN take a deeper ring (NN fills the LDS),
+// NT is already full at 160 KB.
+template <bool A_T, bool B_KN>
+struct RingsPP;
+#ifndef TPS_PP_NN_RING
+#define TPS_PP_NN_RING 64, 3, 32, 4
+#endif
+#ifndef TPS_PP_NT_RING
+#define TPS_PP_NT_RING 64, 2, 64, 3
+#endif
+#ifndef TPS_PP_TN_RING
+#define TPS_PP_TN_RING 32, 4, 32, 4
+#endif
+template <>
+struct RingsPP<false, true> : RingOf<TPS_PP_NN_RING> {};   // 160 KB
+template <>
+struct RingsPP<false, false> : RingOf<TPS_PP_NT_RING> {};  // 160 KB
+template <>
+struct RingsPP<true, true> : RingOf<TPS_PP_TN_RING> {};    // 128 KB
+
+template <bool A_T, bool B_KN, int BM, int BN, int TM, int TN, int WVM, int WVN>
+using CfgPP = Cfg<BM, BN, TM, TN, RingsPP<A_T, B_KN>::BKA, RingsPP<A_T, B_KN>::SA, RingsPP<A_T, B_KN>::BKB,
+                  RingsPP<A_T, B_KN>::SB, WVM, WVN, true>;
+
+
 enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224 };
 
 // Tile shape with the fewest waves of workgroups (ksplit per tile) times
@@ -137,19 +194,23 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
         using Small = Cfg<64, 128, 64, 128, 64, 3, Rings<A_T, B_KN>::BKB, B_KN ? 4 : 3, 2, 2>;
         if (a.M < 256) return launch_cfg<Small, A_T, B_KN, EPI>(fn, a, s);
     }
+    // ping-pong forms: 8 waves, 128 x 64 (2 x 4) or 64 x 112 / 112 x 64
+    using PSq = CfgPP<A_T, B_KN, 256, 256, 256, 256, 2, 4>;
+    using PN224 = CfgPP<A_T, B_KN, 256, 256, 256, 224, 4, 2>;
+    using PM224 = CfgPP<A_T, B_KN, 256, 256, 224, 256, 2, 4>;
     switch (pick_shape(a.M, a.N, SW, true, a.ksplit)) {
         case SHAPE_N224:
-            // SwiGLU: 2 x 2 waves of 128 x 112, gate in wave column 0 and up
-            // in column 1, joined through LDS in the epilogue (1.4 % faster
-            // than 4 x 1 waves holding both halves, which read 45 % more
-            // fragments per MFMA)
-            if constexpr (SW) return launch_cfg<SwiN224, A_T, B_KN, EPI_SWIGLU_X>(fn, a, s);
-            else return launch_cfg<N224, A_T, B_KN, EPI>(fn, a, s);
+            // SwiGLU: gate in wave column 0 and up in column 1, joined
+            // through LDS in the epilogue (interleaved: 2 x 2 waves of
+            // 128 x 112, 1.4 % faster than 4 x 1 waves holding both halves,
+            // which read 45 % more fragments per MFMA)
+            if constexpr (SW) return launch_pp_or<SwiN224, PN224, A_T, B_KN, EPI_SWIGLU_X>(fn, a, s);
+            else return launch_pp_or<N224, PN224, A_T, B_KN, EPI>(fn, a, s);
         case SHAPE_M224:
-            if constexpr (!SW) return launch_cfg<M224, A_T, B_KN, EPI>(fn, a, s);
-            else return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
+            if constexpr (!SW) return launch_pp_or<M224, PM224, A_T, B_KN, EPI>(fn, a, s);
+            else return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);
         default:
-            return launch_cfg<Sq, A_T, B_KN, EPI>(fn, a, s);
+            return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);
     }
 }
 
