@@ -39,9 +39,9 @@ METRIC = "TFLOP/s + % bf16 MFMA peak, Llama-3-70B TP=8 MLP shard fwd+bwd, 1 GPU"
 
 # What each timed product launches (one gemm_kernel instantiation each).
 KERNEL_DESC = {
-    "gemm1_gate_up_swiglu": "gemm_kernel NN, 256x224 tile (112 gate + 112 up columns in separate waves, "
-                            "joined through LDS), SwiGLU epilogue",
-    "gemm2_down_partial": "gemm_kernel NN, 256x256 tile, fp32 store",
+    "gemm1_gate_up_swiglu": "gemm_kernel NN ping-pong, 256x224 tile, 8 waves (112 gate + 112 up columns in "
+                            "separate waves, joined through LDS), SwiGLU epilogue",
+    "gemm2_down_partial": "gemm_kernel NN ping-pong, 256x256 tile, 8 waves, fp32 store",
     "bwd_dz_swiglu": "gemm_kernel NT, 256x224 tile, 8 waves, SwiGLU backward epilogue reading H",
     "bwd_dx_partial": "gemm_kernel NT, 256x256 tile, fp32 store",
     "bwd_dw_gate_up": "gemm_kernel TN, 256x224 tile, 8 waves, fp32 store",
@@ -415,13 +415,18 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     ms_eager = time_fn(regroup, max(reps, 32), warm=4)[0]
     ms = time_graph(regroup, 32)
     moved = 2 * h * (width // t) * 2
-    # context: a plain device copy of the same bytes (contiguous), same graph timing
+    # context: a plain device copy of the same bytes (contiguous), same graph
+    # timing, reading a different slice of the sources as the ranks rotate
+    # (8 slices x 4 sources = 671 MB), so that, like the regroup's, its reads
+    # come from HBM and not from the 256 MB Infinity Cache
     it[0] = 0
+    n_slice = h * (width // t)
 
     def plain_copy():
         i = it[0]
         it[0] += 1
-        dsts[i % 4].view(-1).copy_(srcs[i % 4].view(-1)[: h * (width // t)])
+        k = (i // 4) % t
+        dsts[i % 4].view(-1).copy_(srcs[i % 4].view(-1)[k * n_slice:(k + 1) * n_slice])
 
     ms_copy = time_graph(plain_copy, 32)
     res["qkv_regroup"] = {"ms": round(ms, 5), "ms_eager": round(ms_eager, 5), "bytes": moved,
