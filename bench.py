@@ -89,6 +89,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the oracle CPU baseline runs (0 = skip)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    ap.add_argument("--data", choices=("normal", "zeros", "ints"), default="normal",
+                    help="values of the step's inputs: the seeded synthetic workload (normal, the default), "
+                         "all zeros, or small integers in [-2, 2]; same shapes and kernels (for the power "
+                         "study: the chip's clock under the step depends on the data's switching activity)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device 5 times (scale for HBM byte counters), then exit")
     ap.add_argument("--regroup-only", type=int, default=0, metavar="CALLS",
@@ -168,6 +172,16 @@ def main() -> int:
     d = synth.mlp_inputs(w.seed, N, h, w.F, w.t, "swiglu")
     dY_bits = synth.mlp_bwd_inputs(wb.seed, N, h)["dY"]
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+    if args.data != "normal":
+        # same shapes, other values: all zeros, or integers in [-2, 2]
+        if args.data == "zeros":
+            def alt(shape, seed):
+                return np.zeros(shape, np.uint16)
+        else:
+            def alt(shape, seed):
+                return synth.int_inputs(seed, shape)
+        d = {k: alt(v.shape, 100 + i) for i, (k, v) in enumerate(d.items())}
+        dY_bits = alt(dY_bits.shape, 99)
     X, W_in, W_out, dY = to_dev(d["X"]), to_dev(d["W_in"]), to_dev(d["W_out"]), to_dev(dY_bits)
     bf, f32 = torch.bfloat16, torch.float32
     Z = torch.empty((N, f), dtype=bf, device=dev)
@@ -324,6 +338,21 @@ def main() -> int:
     if chunked:
         kt["gemm2_down_partial_chunked"] = chunked
 
+    # The fp32 epilogue's cost: GEMM2's output shape (512 tiles of 256 x 256,
+    # two waves on 256 CUs) contracted over K = 64, two k32 sub-steps, so a
+    # launch is almost only its prologue and the 128 MiB of fp32 stores; the
+    # per-CU store rate is the output bytes / time / CUs.
+    if not args.no_rows:
+        Zk64, Wk64 = Z[:, :64].contiguous(), W_out[:64].contiguous()
+        ms_st = time_fn(lambda: T.tp_row_linear_partial(Zk64, Wk64, P=P), args.reps)[0]
+        del Zk64, Wk64
+        out_bytes = 4 * N * h
+        kt["gemm2_shape_k64_store_bound"] = {
+            "ms": round(ms_st, 4), "output_bytes": out_bytes,
+            "gbs": round(out_bytes / (ms_st * 1e-3) / 1e9, 1),
+            "per_cu_gbs": round(out_bytes / (ms_st * 1e-3) / 1e9 / props.multi_processor_count, 1)}
+        log(f"[bench] GEMM2 shape at K = 64 (stores): {kt['gemm2_shape_k64_store_bound']}")
+
     # Epilogue fusion, for context: the same products with a plain bf16 store,
     # then the activation (or its derivative) as a separate elementwise pass
     # in eager torch (several kernels). A single ideal pass would move 84 MiB
@@ -380,7 +409,9 @@ def main() -> int:
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "data": {"normal": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+                 "zeros": "all-zero inputs (power study, not the workload)",
+                 "ints": "integers in [-2, 2] (power study, not the workload)"}[args.data],
         "config": {"workload": "llama3-70b-tp8-swiglu-mlp-shard-fwd-bwd", "tokens": N, "h": h,
                    "F": w.F, "t": w.t, "f": f, "step_gflop": round(step_flops / 1e9, 2)},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
