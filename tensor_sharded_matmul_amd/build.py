@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpshard.so")
 SOURCES = ["tpshard.hip", "gemm_nn_store.hip", "gemm_nn_act.hip", "gemm_nn_ce.hip", "gemm_nt_store.hip",
-           "gemm_nt_act.hip", "gemm_tn.hip"]
+           "gemm_nt_act.hip", "gemm_tn.hip", "gemm_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -13,6 +13,7 @@
 #include <utility>
 
 #include "../../include/tpshard.h"
+#include "decode.h"
 #include "gemm_kernel.h"
 
 namespace tps {
@@ -97,6 +98,9 @@ static tp_status check_elems(const char* fn, int64_t rows, int64_t cols) {
 // epilogue family per file, in the gemm_*.hip sources (compiled in parallel).
 template <bool A_T, bool B_KN, int EPI>
 tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s);
+// Decode-sized forward products (gemm_decode.hip).
+template <int EPI>
+tp_status launch_decode(const char* fn, const GemmArgs& a, const DecodePlan& p, void* ws, hipStream_t s);
 
 static GemmArgs make_args(const void* A, const void* B, void* C, int M, int N, int K, int lda, int ldb,
                           int ldc) {
@@ -230,11 +234,16 @@ int device_cus() {
     return v;
 }
 
-// How a product is run: ksplit == 0 means one launch of the tiled kernel;
-// otherwise K is cut into ksplit chunks of kper (a multiple of 64) whose f32
-// partials take `bytes` of workspace and splitk_reduce applies the epilogue.
-//  - Few token rows (M <= 64, NN, the decode shapes): the weight is streamed
-//    from HBM by one split workgroup per CU, in chunks of at least
+// How a product is run: dec.nslab > 0 means the decode kernel (with
+// dec.nsplit > 1, its f32 partials take `bytes` of workspace and
+// splitk_reduce applies the epilogue); else ksplit == 0 means one launch of
+// the tiled kernel; otherwise K is cut into ksplit chunks of kper (a
+// multiple of 64) whose f32 partials take `bytes` of workspace and
+// splitk_reduce applies the epilogue.
+//  - At most 32 token rows (NN): the decode kernel when its slabs x splits
+//    fit one wave of workgroups (decode.h).
+//  - Other few-row products (M <= 64, NN): the weight is streamed from HBM
+//    by one split workgroup per CU, in chunks of at least
 //    TPS_SPLIT_MIN_KPER rows.
 //  - Large products whose 256 x 256 tiles do not fill the CUs once (the
 //    attention projections' N = 1024 or 1280 shard widths): the split count
@@ -253,6 +262,7 @@ int device_cus() {
 struct SplitPlan {
     int ksplit = 0, kper = 0, Nw = 0;
     size_t bytes = 0;
+    DecodePlan dec;
 };
 
 static SplitPlan make_plan(const GemmArgs& a, int Nw, int ksplit_wanted) {
@@ -275,6 +285,14 @@ static SplitPlan plan_split(const GemmArgs& a, bool swiglu, bool nn, bool splitt
     const long long cus = device_cus();
     if (a.M <= 64) {
         if (!nn) return none;
+        const DecodePlan dec = decode_plan(a.M, a.K, Nw, a.ldb, (int)cus);
+        if (dec.nslab > 0) {
+            SplitPlan p = none;
+            p.dec = dec;
+            p.ksplit = dec.nsplit;
+            p.bytes = dec.bytes;
+            return p;
+        }
         const int tm = splitk_tile_m(a.M);
         const long long tiles = (long long)((a.M + tm - 1) / tm) * ((Nw + 127) / 128);
         if (tiles >= 2 * cus || a.K < 2 * TPS_SPLIT_MIN_KPER) return none;
@@ -327,10 +345,35 @@ static size_t need_of(std::initializer_list<SplitPlan> plans) {
 
 // A product with its epilogue, run as plan_of decides; a split product puts
 // its partials in ws (sized by the caller from the same plan).
+// The sum of ksplit f32 partials [ksplit][M][Nw] in ws, with a's epilogue.
+template <int EPI>
+static tp_status launch_reduce(const char* fn, const GemmArgs& a, int ksplit, int Nw, const void* ws,
+                               hipStream_t s) {
+    int S = 1;
+    while (S * kReduceLoads < ksplit && S < 64) S *= 2;
+    const long long quads = (long long)a.M * (a.N / 4);
+    const long long per_block = 4 * (64 / S);
+    const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
+    hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(ws), ksplit, S,
+                       a.M, Nw, a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return TP_OK;
+}
+
 template <bool A_T, bool B_KN, int EPI>
 static tp_status run_gemm(const char* fn, const GemmArgs& a, void* ws, hipStream_t s) {
     if (a.M == 0 || a.N == 0) return TP_OK;
     const SplitPlan plan = plan_of<A_T, B_KN, EPI>(a);
+    if constexpr (reducible<EPI>() && !A_T && B_KN) {
+        if (plan.dec.nslab > 0) {
+            if (plan.dec.nsplit > 1 && ws == nullptr)
+                return fail(TP_ERR_INVALID_ARG, "%s: a split product without workspace", fn);
+            TP_TRY(launch_decode<EPI>(fn, a, plan.dec, ws, s));
+            if (plan.dec.nsplit == 1) return TP_OK;
+            return launch_reduce<EPI>(fn, a, plan.dec.nsplit, plan.Nw, ws, s);
+        }
+    }
     if (plan.ksplit == 0) return launch_gemm<A_T, B_KN, EPI>(fn, a, s);
     if constexpr (reducible<EPI>()) {
         if (ws == nullptr) return fail(TP_ERR_INVALID_ARG, "%s: a split product without workspace", fn);
@@ -343,16 +386,7 @@ static tp_status run_gemm(const char* fn, const GemmArgs& a, void* ws, hipStream
         p.ksplit = plan.ksplit;
         p.kper = plan.kper;
         TP_TRY((launch_gemm<A_T, B_KN, EPI_F32>(fn, p, s)));
-        int S = 1;
-        while (S * kReduceLoads < plan.ksplit && S < 64) S *= 2;
-        const long long quads = (long long)a.M * (a.N / 4);
-        const long long per_block = 4 * (64 / S);
-        const unsigned blocks = (unsigned)std::min<long long>((quads + per_block - 1) / per_block, 8192);
-        hipLaunchKernelGGL(splitk_reduce<EPI>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(ws),
-                           plan.ksplit, S, a.M, plan.Nw, a.N, a.C, a.ldc, a.C2, a.ldc2, a.f, a.accumulate);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-        return TP_OK;
+        return launch_reduce<EPI>(fn, a, plan.ksplit, plan.Nw, p.C, s);
     } else {
         return fail(TP_ERR_UNSUPPORTED, "%s: split of an unsplittable epilogue", fn);
     }

@@ -66,3 +66,18 @@ def bf16_ulps(got_bits: np.ndarray, want: np.ndarray) -> int:
         return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
 
     return int(np.max(np.abs(line(g) - line(w)))) if g.size else 0
+
+
+def assert_elementwise(got, want, label, rel=2.0 ** -8, abs_frac=1e-6):
+    """|got - want| <= rel |want| + abs_frac max|want| for every element: one
+    bf16 rounding (2^-9 relative) plus the f32 evaluation of the activation;
+    the absolute part covers tails where f32 flushes what bf16 could hold."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape
+    tol = rel * np.abs(want) + abs_frac * np.max(np.abs(want))
+    bad = ~(np.abs(got - want) <= tol)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{label}: {int(bad.sum())} elements off, first at {tuple(i)}: "
+                             f"got {got[tuple(i)]!r}, want {want[tuple(i)]!r}")

@@ -151,8 +151,8 @@ def test_gemm_entry_points_validate_before_launch():
 # of its workspace query.
 WS_CASES = {
     "tp_col_linear": (16, 8192, 1280, 0),
-    "tp_row_linear_partial": (16, 1024, 8192),
-    "tp_row_linear_partial_chunked": (48, 1024, 8192, 3),
+    "tp_row_linear_partial": (16, 8192, 8192),
+    "tp_row_linear_partial_chunked": (48, 8192, 8192, 3),
     "tp_mlp_shard_fwd": (16, 8192, 3584, 2),
     "tp_row_linear_bwd": (4096, 1024, 8192),
     "tp_vocab_ce_fwd": (4096, 8192, 16128),
@@ -181,6 +181,17 @@ def test_workspace_query_values():
     # each; the embedding stamps: 4 bytes per table row
     n = T.workspace_size("tp_col_linear", 16, 8192, 1280, 0)
     assert n % (16 * 1280 * 4) == 0 and 2 <= n // (16 * 1280 * 4) <= 64
+    # decode plans (256 CUs): 32-column slabs when no K split is needed (at
+    # most 48 k-blocks of 32 rows per workgroup at 16 tokens, 32 at 32), else
+    # 64-column slabs (24 blocks at 16 or 32 tokens). The QKV product at 16
+    # tokens: 20 slabs in 12 K splits (240 workgroups); W_O: 256 slabs, no
+    # split; the 32-row QKV product over K = 2048: 20 slabs x 8 splits
+    assert n == 12 * 16 * 1280 * 4
+    assert T.workspace_size("tp_row_linear_partial", 16, 1024, 8192) == 0
+    assert T.workspace_size("tp_row_linear_partial", 32, 1024, 8192) == 0
+    assert T.workspace_size("tp_col_linear", 16, 256, 4096, 2) == 0   # SwiGLU, 8192 weight columns: no split
+    assert T.workspace_size("tp_col_linear", 32, 2048, 1280, 0) == 8 * 32 * 1280 * 4
+    assert T.workspace_size("tp_col_linear", 32, 8192, 1280, 0) > 0
     assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 2 * (16128 // 224) * 12
     assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
     # products with enough output tiles need none

@@ -31,7 +31,7 @@ import torch
 import oracle as O
 import synth
 import tensor_sharded_matmul_amd as T
-from gpu_util import bits, f64, rne_bf16_bits, to_dev
+from gpu_util import assert_elementwise, bits, f64, rne_bf16_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -51,21 +51,6 @@ def _canary(shape, dtype):
 
 def _untouched(big, n):
     return bool(torch.all(big[n:] == SENTINEL))
-
-
-def assert_elementwise(got, want, label, rel=2.0 ** -8, abs_frac=1e-6):
-    """|got - want| <= rel |want| + abs_frac max|want| for every element: one
-    bf16 rounding (2^-9 relative) plus the f32 evaluation of the activation;
-    the absolute part covers tails where f32 flushes what bf16 could hold."""
-    got = np.asarray(got, np.float64)
-    want = np.asarray(want, np.float64)
-    assert got.shape == want.shape
-    tol = rel * np.abs(want) + abs_frac * np.max(np.abs(want))
-    bad = ~(np.abs(got - want) <= tol)
-    if bad.any():
-        i = np.argwhere(bad)[0]
-        raise AssertionError(f"{label}: {int(bad.sum())} elements off, first at {tuple(i)}: "
-                             f"got {got[tuple(i)]!r}, want {want[tuple(i)]!r}")
 
 
 def test_gemm1_swiglu_nn_256x224_split_waves():
