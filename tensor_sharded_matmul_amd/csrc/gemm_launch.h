@@ -145,11 +145,13 @@ using CfgPP = Cfg<BM, BN, TM, TN, RingsPP<A_T, B_KN>::BKA, RingsPP<A_T, B_KN>::S
                   RingsPP<A_T, B_KN>::SB, WVM, WVN, true>;
 
 
-enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224 };
+enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224, SHAPE_N160 };
 
 // Tile shape with the fewest waves of workgroups (ksplit per tile) times
-// tile area, i.e. the least padded work per CU.
-inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int ksplit) {
+// tile area, i.e. the least padded work per CU. 256 x 160 tiles (weight
+// gradients only) fill the 256 CUs with the 1280-wide QKV shard of
+// Llama-3-70B at t = 8 (32 x 8 tiles against 32 x 6 of 256 x 224).
+inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int ksplit, bool allow_n160 = false) {
     const long long cus = device_cus();
     auto cost = [&](int tm, int tnz, int area) {
         const long long t = (long long)((M + tm - 1) / tm) * ((Nout + tnz - 1) / tnz) * ksplit;
@@ -162,6 +164,10 @@ inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int kspli
     if (allow_m224 && !swiglu) {
         const long long c_m = cost(224, 256, 224 * 256);
         if (c_m < c_best) { best = SHAPE_M224; c_best = c_m; }
+    }
+    if (allow_n160 && !swiglu) {
+        const long long c_n160 = cost(256, 160, 256 * 160);
+        if (c_n160 < c_best) { best = SHAPE_N160; c_best = c_n160; }
     }
     return best;
 }
@@ -198,7 +204,15 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
     using PSq = CfgPP<A_T, B_KN, 256, 256, 256, 256, 2, 4>;
     using PN224 = CfgPP<A_T, B_KN, 256, 256, 256, 224, 4, 2>;
     using PM224 = CfgPP<A_T, B_KN, 256, 256, 224, 256, 2, 4>;
-    switch (pick_shape(a.M, a.N, SW, true, a.ksplit)) {
+    constexpr bool TN_F32 = A_T && B_KN && EPI == EPI_F32;
+    switch (pick_shape(a.M, a.N, SW, true, a.ksplit, TN_F32)) {
+        case SHAPE_N160:
+            if constexpr (TN_F32) {
+                // 8 waves of 64 x 80; loads stay 256 columns wide
+                using N160 = CfgOf<A_T, B_KN, 256, 256, 256, 160, 4, 2>;
+                return launch_cfg<N160, A_T, B_KN, EPI>(fn, a, s);
+            }
+            return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);
         case SHAPE_N224:
             // SwiGLU: gate in wave column 0 and up in column 1, joined
             // through LDS in the epilogue (interleaved: 2 x 2 waves of
