@@ -98,6 +98,12 @@ def parse():
     ap.add_argument("--regroup-only", type=int, default=0, metavar="CALLS",
                     help="only run the fused-QKV regroup CALLS times (4 rotated sources, ranks 0..7; "
                          "for profiling), then exit")
+    ap.add_argument("--attn-prefill-only", type=int, default=0, metavar="CALLS",
+                    help="only run the six attention-projection products of one Llama-3-70B rank at 4096 "
+                         "tokens (and the vendor BLAS on the same products) CALLS times (for profiling), then exit")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="only run the MFMA rate probe (bf16 16x16x32 MFMAs on register operands, no memory "
+                         "traffic; random and all-zero data) and print its JSON lines, then exit")
     ap.add_argument("--decode-only", type=int, default=0, metavar="CALLS",
                     help="only run the decode-sized (16 tokens) QKV and W_O products of the Llama-3-70B "
                          "attention shard CALLS times (16 rotated weight copies; for profiling), then exit")
@@ -119,6 +125,10 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.mfma_rate:
+        for r in mfma_rate():
+            print(json.dumps(r), flush=True)
+        return 0
     T.load()
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -140,6 +150,32 @@ def main() -> int:
             T.tp_qkv_regroup(srcs[i % 4], q.n_h, q.n_kv, q.d_h, q.t, (i // 4) % q.t, W_r=dsts[i % 4])
         torch.cuda.synchronize()
         log(f"[bench] regrouped {args.regroup_only} times")
+        return 0
+    if args.attn_prefill_only:
+        q = synth.WORKLOADS["llama70b_qkv_t8"]
+        wq, wo, Np = (q.n_h + 2 * q.n_kv) * q.d_h // q.t, q.n_h * q.d_h // q.t, 4096
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(q.seed)
+        rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+        X, Wr, O, WO, dQ, dY = rnd(Np, q.h), rnd(q.h, wq), rnd(Np, wo), rnd(wo, q.h), rnd(Np, wq), rnd(Np, q.h)
+        f32 = torch.float32
+        Y = torch.empty((Np, wq), device=dev, dtype=torch.bfloat16)
+        P, dX = torch.empty((Np, q.h), device=dev, dtype=f32), torch.empty((Np, q.h), device=dev, dtype=f32)
+        dW, dWO = torch.empty((q.h, wq), device=dev, dtype=f32), torch.empty((wo, q.h), device=dev, dtype=f32)
+        dO = torch.empty((Np, wo), device=dev, dtype=torch.bfloat16)
+        # the vendor BLAS on the same products, bf16 outputs, as plain NN
+        # products of contiguous operands (the transposes made beforehand)
+        Wrt, Xt, WOt, Ot = Wr.t().contiguous(), X.t().contiguous(), WO.t().contiguous(), O.t().contiguous()
+        vend = ((X, Wr), (O, WO), (dQ, Wrt), (Xt, dQ), (dY, WOt), (Ot, dY))
+        for _ in range(args.attn_prefill_only):
+            T.tp_col_linear(X, Wr, "none", Y=Y)
+            T.tp_row_linear_partial(O, WO, P=P)
+            T.tp_col_linear_bwd(X, Wr, dQ, dX_part=dX, dW=dW)
+            T.tp_row_linear_bwd(O, WO, dY, dZ=dO, dW=dWO)
+            for a_, b_ in vend:
+                torch.matmul(a_, b_)
+        torch.cuda.synchronize()
+        log(f"[bench] attention prefill products run {args.attn_prefill_only} times")
         return 0
     if args.decode_only:
         q = synth.WORKLOADS["llama70b_qkv_t8"]
@@ -399,6 +435,14 @@ def main() -> int:
         rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, args.reps))
         rows["vendor_gemm_reference"] = vendor_reference(torch, dev, time_fn, args.reps, N, h, f)
     torch.cuda.synchronize()
+    if not args.no_rows:
+        # the matrix cores' sustained rate on this GPU with no memory traffic
+        # (random and all-zero operands), beside the step's rate
+        mr = mfma_rate()
+        med = {k: float(np.median([r["tflops"] for r in mr if r["data"] == k])) for k in ("random", "zeros")}
+        rows["mfma_rate_no_memory"] = {"random_tflops": round(med["random"], 1), "zeros_tflops": round(med["zeros"], 1),
+                                       "step_frac_of_random": round(value / med["random"], 3)}
+        log(f"[bench] MFMA rate without memory traffic: {rows['mfma_rate_no_memory']}")
 
     # ---------------- CPU baseline: the oracle on a token sample ----------------
     cpu = None
@@ -557,6 +601,11 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
                                    "gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
                                    "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
                                    "blas_ms": round(ms_blas, 4)}
+    # context for the launch-bound rows: a kernel that does almost nothing
+    # (a 16-element add), replayed from the same kind of graph
+    tiny = torch.zeros(16, device=dev)
+    res["graph_launch_floor"] = {"us_per_kernel": round(1000 * time_graph(lambda: tiny.add_(1.0), 16), 2)}
+    del tiny
     del Wrs, WOs, X, O, dQKV, dY, W_r, W_O
 
     # --- Llama-3-70B vocab-parallel LM head + fused cross-entropy, one shard of 8 ---
@@ -652,6 +701,19 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     log(f"[bench] vendor BLAS attention projections: fwd {res['attn_fwd_total']['tflops']}, "
         f"bwd {res['attn_bwd_total']['tflops']} TFLOP/s")
     return res
+
+
+def mfma_rate(iters=20000, reps=3):
+    """Run the MFMA rate probe built beside the library (a child process on
+    the same GPU); returns its records {data, rep, ms, tflops}."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", "mfma_rate")
+    if not os.path.exists(exe):
+        raise RuntimeError(f"{exe} is not built; run `python -m tensor_sharded_matmul_amd.build`")
+    r = subprocess.run([exe, str(iters), str(reps)], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        raise RuntimeError(f"mfma_rate failed ({r.returncode}): {r.stderr.strip()[-500:]}")
+    return [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
 
 
 def cpu_baseline(d, dY_bits, n_tok, synth, np):

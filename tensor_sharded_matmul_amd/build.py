@@ -16,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpshard.so")
+# the MFMA rate probe (bench.py --mfma-rate): a standalone executable
+PROBE_SRC, PROBE = "mfma_rate.hip", os.path.join(HERE, "mfma_rate")
 SOURCES = ["tpshard.hip", "gemm_nn_store.hip", "gemm_nn_act.hip", "gemm_nn_ce.hip", "gemm_nt_store.hip",
            "gemm_nt_act.hip", "gemm_tn.hip", "gemm_decode.hip"]
 ARCH = "gfx950"
@@ -100,6 +102,11 @@ def build(asm_dir: str | None = None, verbose: bool = True) -> str:
         print("[build]", " ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    cmd = [hipcc()] + flags() + [os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 
