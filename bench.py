@@ -39,8 +39,8 @@ METRIC = "TFLOP/s + % bf16 MFMA peak, Llama-3-70B TP=8 MLP shard fwd+bwd, 1 GPU"
 
 # What each timed product launches (one gemm_kernel instantiation each).
 KERNEL_DESC = {
-    "gemm1_gate_up_swiglu": "gemm_kernel NN ping-pong, 256x224 tile, 8 waves (112 gate + 112 up columns in "
-                            "separate waves, joined through LDS), SwiGLU epilogue",
+    "gemm1_gate_up_swiglu": "gemm_kernel NN ping-pong, 256x256 tile (128 gate + 128 up columns), 8 waves, "
+                            "SwiGLU epilogue",
     "gemm2_down_partial": "gemm_kernel NN ping-pong, 256x256 tile, 8 waves, fp32 store",
     "bwd_dz_swiglu": "gemm_kernel NT, 256x224 tile, 8 waves, SwiGLU backward epilogue reading H",
     "bwd_dx_partial": "gemm_kernel NT, 256x256 tile, fp32 store",

@@ -41,10 +41,8 @@
 //        transposes 4x4 blocks of 16-bit values across each 16-lane group,
 //        giving every lane 4 consecutive k of one column.
 //    so the MFMA inner loop is the same for every layout.
-//  * SwiGLU loads the B tile as [gate | up] halves over the same F indices.
-//    In the 256 x 224 tile wave column 0 computes the gate half and column 1
-//    the up half, and the epilogue joins them through LDS (EPI_SWIGLU_X);
-//    other tiles hold both halves in every wave (EPI_SWIGLU).
+//  * SwiGLU loads the B tile as [gate | up] halves over the same F indices;
+//    every wave holds both halves of its output columns (EPI_SWIGLU).
 //  * Workgroup -> tile mapping is XCD-aware: the hardware deals workgroups
 //    round-robin over the 8 XCDs, so consecutive blocks of tiles are mapped
 //    to one XCD (sharing its L2), grouped GROUP_M tile rows at a time.
@@ -89,7 +87,6 @@ enum Epi : int {
     EPI_SWIGLU_BWD = 5, // C bf16 = [acc*u*SiLU'(g) | acc*SiLU(g)], aux = [g|u]
     EPI_CE_STATS = 6,   // logits -> per (row, wave column block) {max, sum exp(z - max), z_target}
     EPI_CE_GRAD = 7,    // C bf16 = (exp(acc - m) / S - [col = target]) * dloss, per row
-    EPI_SWIGLU_X = 8,   // as EPI_SWIGLU, gate and up computed by different waves (exchanged through LDS)
 };
 
 struct GemmArgs {
@@ -684,63 +681,6 @@ __device__ __forceinline__ void epilogue_f32_store_acc(const f32x4_t (&acc)[MI][
     });
 }
 
-// SwiGLU with gate and up in different waves (EPI_SWIGLU_X): the wave of
-// column 1 of the wave grid holds the up values of the outputs whose gate
-// values the wave of column 0 holds (same lanes, same blocks). The up waves
-// write their accumulators to LDS (the operand ring, idle after the k-loop)
-// and store U to the saved H; the gate waves read them back, form
-// Z = SiLU(G) U and store Z and G.
-template <int MI, int NI>
-__device__ __forceinline__ void epilogue_swx_gate(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb, int nb,
-                                                  uint32_t xch) {
-    typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
-    static_for<0, MI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        const int m = mb + i * 16;
-        if (m < args.M) {
-            uint16_t* crow = reinterpret_cast<uint16_t*>(args.C) + (size_t)m * args.ldc;
-            static_for<0, NI>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                const int n = nb + j * 16;
-                if (n < args.N) {
-                    const f32x4_t g = acc[i][j];
-                    const f32x4_t u = *reinterpret_cast<const lds_f32x4*>((uintptr_t)(xch + (i * NI + j) * 1024));
-                    float z[4];
-                    static_for<0, 4>([&](auto rc) {
-                        constexpr int r = decltype(rc)::value;
-                        z[r] = g[r] * sigmoid_f(g[r]) * u[r];
-                    });
-                    *reinterpret_cast<u32x2_t*>(crow + n) = pack4(z[0], z[1], z[2], z[3]);
-                    if (args.C2)
-                        *reinterpret_cast<u32x2_t*>(args.C2 + (size_t)m * args.ldc2 + n) = pack4(g[0], g[1], g[2], g[3]);
-                }
-            });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    });
-}
-
-template <int MI, int NI>
-__device__ __forceinline__ void epilogue_swx_up(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb, int nb) {
-    if (!args.C2) return;
-    static_for<0, MI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        const int m = mb + i * 16;
-        if (m < args.M) {
-            uint16_t* hrow = args.C2 + (size_t)m * args.ldc2 + args.f;
-            static_for<0, NI>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                const int n = nb + j * 16;
-                if (n < args.N) {
-                    const f32x4_t u = acc[i][j];
-                    *reinterpret_cast<u32x2_t*>(hrow + n) = pack4(u[0], u[1], u[2], u[3]);
-                }
-            });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    });
-}
-
 // ---------------------------------------------------------------------------
 // Tile configuration.
 //   BM x BN   loaded operand tiles (LDS); TM x TN computed tile (TM <= BM,
@@ -826,8 +766,7 @@ gemm_kernel(const GemmArgs args) {
     constexpr int WAVES_M = CF::WAVES_M, WAVES_N = CF::WAVES_N;
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr bool SWIGLU = (EPI == EPI_SWIGLU);
-    constexpr bool SWX = (EPI == EPI_SWIGLU_X);      // gate and up in different wave columns
-    constexpr bool GATEUP = SWIGLU || SWX;           // B tile = [gate | up] halves
+    constexpr bool GATEUP = SWIGLU;                  // B tile = [gate | up] halves
     constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
     constexpr int MI = WM / 16, NI = WN / 16;
     constexpr int PA = BKA / 32, PB = BKB / 32;     // k32 sub-steps per stage
@@ -837,7 +776,6 @@ gemm_kernel(const GemmArgs args) {
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert((BKA == 32 || BKA == 64) && (BKB == 32 || BKB == 64), "stages of 32 or 64 k-rows");
     static_assert(!SWIGLU || (NI % 2 == 0 && B_KN && WN % 32 == 0), "SwiGLU needs an even gate/up split");
-    static_assert(!SWX || (WAVES_N == 2 && B_KN && WN <= BN / 2), "gate / up wave columns");
     static_assert(SA >= 2 && SB >= 2, "at least two stages per ring");
     static_assert(SA * A_STAGE + SB * B_STAGE <= 160 * 1024, "gfx950 LDS is 160 KB");
 
@@ -926,8 +864,6 @@ gemm_kernel(const GemmArgs args) {
     auto bcol = [&](int j) -> int {
         if constexpr (SWIGLU) {
             return j < NI / 2 ? wn * (WN / 2) + 16 * j : BN / 2 + wn * (WN / 2) + 16 * (j - NI / 2);
-        } else if constexpr (SWX) {
-            return wn * (BN / 2) + 16 * j;
         } else {
             return wn * WN + 16 * j;
         }
@@ -1307,27 +1243,8 @@ gemm_kernel(const GemmArgs args) {
 
     const int lr = lane & 15, lq = lane >> 4;
     const int mb = m0 + wm * WM + lr;
-    const int nb = n0 + (SWX ? 0 : wn * (SWIGLU ? WN / 2 : WN)) + lq * 4;
-    if constexpr (SWX) {
-        // every wave is done with the ring; the up waves put their
-        // accumulators there ([wave row][block][lane], 16 bytes per lane)
-        constexpr int XBYTES = WAVES_M * MI * NI * 64 * 16;
-        static_assert(XBYTES <= SA * A_STAGE + SB * B_STAGE, "the exchange fits the ring");
-        const uint32_t xch = lds_addr(smem) + (uint32_t)(wm * MI * NI * 1024 + lane * 16);
-        __syncthreads();
-        if (wn == 1) {
-            typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
-            static_for<0, MI>([&](auto ic) {
-                static_for<0, NI>([&](auto jc) {
-                    constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-                    *reinterpret_cast<lds_f32x4*>((uintptr_t)(xch + (i * NI + j) * 1024)) = acc[i][j];
-                });
-            });
-        }
-        __syncthreads();
-        if (wn == 0) epilogue_swx_gate<MI, NI>(acc, args, mb, nb, xch);
-        else epilogue_swx_up<MI, NI>(acc, args, mb, nb);
-    } else if constexpr (EPI == EPI_F32 && !PP) {  // split-K partials are plain fp32 stores
+    const int nb = n0 + wn * (SWIGLU ? WN / 2 : WN) + lq * 4;
+    if constexpr (EPI == EPI_F32 && !PP) {  // split-K partials are plain fp32 stores
         GemmArgs part = args;
         if (args.ksplit > 1) {
             part.C = reinterpret_cast<float*>(args.C) + (size_t)split * args.M * args.ldc;

@@ -52,7 +52,7 @@ inline tp_status launch_pp_or(const char* fn, const GemmArgs& a, hipStream_t s) 
 
 template <class CF, bool A_T, bool B_KN, int EPI>
 inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
-    constexpr int TNZ = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_X) ? CF::TN / 2 : CF::TN;
+    constexpr int TNZ = EPI == EPI_SWIGLU ? CF::TN / 2 : CF::TN;
     const long long tiles = (long long)((a.M + CF::TM - 1) / CF::TM) * ((a.N + TNZ - 1) / TNZ) * a.ksplit;
     if (tiles == 0) return TP_OK;
     if (tiles > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tiles", fn);
@@ -150,22 +150,30 @@ enum Shape { SHAPE_SQ, SHAPE_N224, SHAPE_M224, SHAPE_N160 };
 // Tile shape with the fewest waves of workgroups (ksplit per tile) times
 // tile area, i.e. the least padded work per CU. 256 x 160 tiles (weight
 // gradients only) fill the 256 CUs with the 1280-wide QKV shard of
-// Llama-3-70B at t = 8 (32 x 8 tiles against 32 x 6 of 256 x 224).
+// Llama-3-70B at t = 8 (32 x 8 tiles against 32 x 6 of 256 x 224). The
+// SwiGLU forward always takes 256 x 256 tiles (128 gate + 128 up columns,
+// both halves in every wave; a 256 x 224 tile has 112 + 112 and never needs
+// fewer waves): on the Llama-3-70B GEMM1, 448 tiles against 512 in two
+// waves, measured 4.6 % faster than 256 x 224 tiles with gate and up in
+// separate waves (0.344 against 0.361 ms, interleaved runs). The other
+// products keep the area rule (256 x 256 on the same wave count measured
+// 1-10 % slower for dZ and the weight gradients).
 inline Shape pick_shape(int M, int Nout, bool swiglu, bool allow_m224, int ksplit, bool allow_n160 = false) {
+    if (swiglu) return SHAPE_SQ;
     const long long cus = device_cus();
     auto cost = [&](int tm, int tnz, int area) {
         const long long t = (long long)((M + tm - 1) / tm) * ((Nout + tnz - 1) / tnz) * ksplit;
         return ((t + cus - 1) / cus) * area;
     };
     Shape best = SHAPE_SQ;
-    long long c_best = cost(256, swiglu ? 128 : 256, 256 * 256);
-    const long long c_n = cost(256, swiglu ? 112 : 224, 256 * 224);
+    long long c_best = cost(256, 256, 256 * 256);
+    const long long c_n = cost(256, 224, 256 * 224);
     if (c_n < c_best) { best = SHAPE_N224; c_best = c_n; }
-    if (allow_m224 && !swiglu) {
+    if (allow_m224) {
         const long long c_m = cost(224, 256, 224 * 256);
         if (c_m < c_best) { best = SHAPE_M224; c_best = c_m; }
     }
-    if (allow_n160 && !swiglu) {
+    if (allow_n160) {
         const long long c_n160 = cost(256, 160, 256 * 160);
         if (c_n160 < c_best) { best = SHAPE_N160; c_best = c_n160; }
     }
@@ -185,7 +193,6 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
     using Sq = CfgOf<A_T, B_KN, 256, 256, 256, 256, WM_SQ, WN_SQ>;
     using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, (A_T || !B_KN) ? 4 : 2, 2>;
     using M224 = CfgOf<A_T, B_KN, 256, 256, 224, 256, 2, A_T ? 4 : 2>;
-    using SwiN224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;  // SwiGLU: 112 gate + 112 up columns
     if constexpr (!A_T && B_KN && EPI == EPI_F32) {
         // split-K partials of a product with few token rows (decode): the
         // weight streams from HBM through a deep ring of 32-row stages, and
@@ -214,12 +221,8 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
             }
             return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);
         case SHAPE_N224:
-            // SwiGLU: gate in wave column 0 and up in column 1, joined
-            // through LDS in the epilogue (interleaved: 2 x 2 waves of
-            // 128 x 112, 1.4 % faster than 4 x 1 waves holding both halves,
-            // which read 45 % more fragments per MFMA)
-            if constexpr (SW) return launch_pp_or<SwiN224, PN224, A_T, B_KN, EPI_SWIGLU_X>(fn, a, s);
-            else return launch_pp_or<N224, PN224, A_T, B_KN, EPI>(fn, a, s);
+            if constexpr (!SW) return launch_pp_or<N224, PN224, A_T, B_KN, EPI>(fn, a, s);
+            else return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);
         case SHAPE_M224:
             if constexpr (!SW) return launch_pp_or<M224, PM224, A_T, B_KN, EPI>(fn, a, s);
             else return launch_pp_or<Sq, PSq, A_T, B_KN, EPI>(fn, a, s);

@@ -4,12 +4,13 @@ whose tile counts select exactly those kernels.
 
 The tile of a product is chosen from its output shape alone (the fewest waves
 of workgroups over the 256 CUs times the tile area, 256 x 256 against
-256 x 224 and 224 x 256); the contraction length does not enter. So each case
+256 x 224 and 224 x 256; always 256 x 256 for the SwiGLU forward); the
+contraction length does not enter. So each case
 keeps the step's output shape (or one with the same choice) and shortens K
 where that keeps the oracle fast:
 
   kernel launched by the step          case here (M x N output, K)      tiles
-  NN 256x224, SwiGLU in split waves    X W_gu   4096 x 3584 (2f=7168), 256   512 (2 waves)
+  NN 256x256, SwiGLU (+H)              X W_gu   4096 x 3584 (2f=7168), 256   448 (2 waves)
   NN 256x256, fp32 store (GEMM2)       Z W_d    4096 x 8192, 256             512
   NN 256x256, GeLU (+H)                X A      4096 x 8192, 256             512
   NT 256x224, SwiGLU' from H (dZ)      dY W_d^T 4096 x 3584, 256             256 (1 wave)
@@ -53,7 +54,7 @@ def _untouched(big, n):
     return bool(torch.all(big[n:] == SENTINEL))
 
 
-def test_gemm1_swiglu_nn_256x224_split_waves():
+def test_gemm1_swiglu_nn_256x256():
     N, h, f = 4096, 256, 3584
     Xb, X = _ints(201, (N, h), scale=1 / 16)      # G, U = integers / 16: SiLU sees O(1)
     Wb, W = _ints(202, (h, 2 * f))
