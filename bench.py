@@ -51,12 +51,13 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 
 
 def kernel_sources_sha() -> str:
-    """Hash of the kernel sources, to tell whether recorded counters are current."""
+    """Hash of the library's kernel sources (not the MFMA rate probe beside
+    them), to tell whether recorded counters are current."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip")):
+        if f.endswith((".h", ".hip")) and f != "mfma_rate.hip":
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -218,6 +219,8 @@ def main() -> int:
                 return synth.int_inputs(seed, shape)
         d = {k: alt(v.shape, 100 + i) for i, (k, v) in enumerate(d.items())}
         dY_bits = alt(dY_bits.shape, 99)
+    input_digests = {k: synth.digest(d[k]) for k in ("X", "W_in", "W_out")}
+    input_digests["dY"] = synth.digest(dY_bits)
     X, W_in, W_out, dY = to_dev(d["X"]), to_dev(d["W_in"]), to_dev(d["W_out"]), to_dev(dY_bits)
     bf, f32 = torch.bfloat16, torch.float32
     Z = torch.empty((N, f), dtype=bf, device=dev)
@@ -439,9 +442,12 @@ def main() -> int:
         # the matrix cores' sustained rate on this GPU with no memory traffic
         # (random and all-zero operands), beside the step's rate
         mr = mfma_rate()
-        med = {k: float(np.median([r["tflops"] for r in mr if r["data"] == k])) for k in ("random", "zeros")}
+        med = {k: float(np.median([r["tflops"] for r in mr if r.get("data") == k])) for k in ("random", "zeros")}
         rows["mfma_rate_no_memory"] = {"random_tflops": round(med["random"], 1), "zeros_tflops": round(med["zeros"], 1),
                                        "step_frac_of_random": round(value / med["random"], 3)}
+        clk = device_clock(mr)
+        if clk:
+            rows["mfma_rate_no_memory"]["device_max_sclk_mhz"] = clk["max_sclk_mhz"]
         log(f"[bench] MFMA rate without memory traffic: {rows['mfma_rate_no_memory']}")
 
     # ---------------- CPU baseline: the oracle on a token sample ----------------
@@ -457,7 +463,9 @@ def main() -> int:
                  "zeros": "all-zero inputs (power study, not the workload)",
                  "ints": "integers in [-2, 2] (power study, not the workload)"}[args.data],
         "config": {"workload": "llama3-70b-tp8-swiglu-mlp-shard-fwd-bwd", "tokens": N, "h": h,
-                   "F": w.F, "t": w.t, "f": f, "step_gflop": round(step_flops / 1e9, 2)},
+                   "F": w.F, "t": w.t, "f": f, "step_gflop": round(step_flops / 1e9, 2),
+                   # SHA-256 (first 16 hex digits) of the bf16 inputs, to identify the data
+                   "input_digests": input_digests},
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -714,6 +722,11 @@ def mfma_rate(iters=20000, reps=3):
     if r.returncode != 0:
         raise RuntimeError(f"mfma_rate failed ({r.returncode}): {r.stderr.strip()[-500:]}")
     return [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+
+
+def device_clock(records):
+    """The CU count and peak engine clock the probe read from the runtime."""
+    return next((r for r in records if "max_sclk_mhz" in r), None)
 
 
 def cpu_baseline(d, dY_bits, n_tok, synth, np):

@@ -5,7 +5,8 @@
 // wave then runs 16 independent accumulators through `iters` rounds of 32
 // MFMAs whose operands rotate over the fragments, so that the matrix core
 // sees changing data as in a GEMM's k-loop. One workgroup of 4 waves per
-// CU-slot, 1024 workgroups. Prints one JSON line per timed launch.
+// CU-slot, 1024 workgroups. Prints the device's CU count and peak clock,
+// then one JSON line per timed launch.
 //
 // Usage: mfma_rate [iters] [reps]
 #include <hip/hip_runtime.h>
@@ -66,6 +67,14 @@ int main(int argc, char** argv) {
         fprintf(stderr, "usage: mfma_rate [iters >= 4] [reps >= 1]\n");
         return 2;
     }
+    // the device's compute units and peak engine clock, as the runtime reports them
+    int dev = 0, cus = 0, clk_khz = 0;
+    CHECK(hipGetDevice(&dev));
+    CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    CHECK(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeClockRate, dev));
+    printf("{\"cus\": %d, \"max_sclk_mhz\": %d, \"bf16_dense_peak_tflops\": %.1f}\n", cus, clk_khz / 1000,
+           (double)cus * clk_khz * 1e3 * 4096 / 1e12);
+    fflush(stdout);
     const size_t frags = (size_t)kBlocks * kThreads * 16;  // 16 fragments of 16 bytes per lane
     std::vector<uint16_t> host(frags * 8);
     bf16x8_t* src = nullptr;
