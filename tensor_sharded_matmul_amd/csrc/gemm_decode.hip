@@ -37,24 +37,19 @@ struct DecGeom {
     static_assert(WAVE_LDS >= MT * SC * 4, "a wave's slots hold its accumulators at the end");
 };
 
-// SWCOLS: the slab's SC B columns are SC/2 gate columns j0.. and the SC/2 up
-// columns f + j0.. (SwiGLU), and an fp32 output (the split partials) goes to
-// those same columns; otherwise slab s is columns SC s .. SC s + SC - 1.
-// Workgroup -> (slab, split). With 32-column slabs two neighbouring slabs
-// share every 128-byte line of the weight: the pair (2p, 2p + 1) of a split
-// runs on one XCD (the hardware deals workgroups round-robin over the 8
-// XCDs), as blocks b and b + 8, so that the line is fetched into that XCD's
-// L2 once (measured: the 16-token W_O product of Llama-3-70B at t = 8, 256
-// slabs, 7.6 us unpaired, 5.7 us paired). A tail of fewer than 16
-// workgroups keeps the plain order.
+// Workgroup -> (slab, split). 32-column slabs run unsplit, and two
+// neighbouring slabs share every 128-byte line of the weight: slabs 16q + 2x
+// and 16q + 2x + 1 go to workgroups b = 16q + x and b + 8, which the hardware
+// (dealing workgroups round-robin over the 8 XCDs) places on the same XCD, so
+// that the line is fetched into that XCD's L2 once (measured: the 16-token
+// W_O product of Llama-3-70B at t = 8, 256 slabs, 7.6 us unpaired, 5.7 us
+// paired). A tail of fewer than 16 slabs keeps the plain order.
 template <int SC>
 __device__ __forceinline__ void dec_unit(int b, int nslab, int nsplit, int& slab, int& split) {
-    const int W = nslab * nsplit;
-    if (SC == 32 && b < W / 16 * 16) {
-        const int x = b & 7, i = b >> 3;
-        const int k = 8 * (i >> 1) + x, h = i & 1;  // pair k, half h
-        slab = 2 * (k / nsplit) + h;
-        split = k % nsplit;
+    if (SC == 32 && nsplit == 1 && b < nslab / 16 * 16) {
+        const int i = b >> 3;
+        slab = 16 * (i >> 1) + 2 * (b & 7) + (i & 1);
+        split = 0;
     } else {
         slab = b / nsplit;
         split = b % nsplit;
@@ -62,7 +57,10 @@ __device__ __forceinline__ void dec_unit(int b, int nslab, int nsplit, int& slab
 }
 
 // MODE 0: one split, the epilogue EPI stores the output; MODE 1: fp32
-// partials to the workspace, for the split reduction.
+// partials to the workspace, for the split reduction. SWCOLS: the slab's SC
+// B columns are SC/2 gate columns j0.. and the SC/2 up columns f + j0..
+// (SwiGLU), and an fp32 output (the split partials) goes to those same
+// columns; otherwise slab s is columns SC s .. SC s + SC - 1.
 template <int MT, int SC, int EPI, bool SWCOLS, int MODE>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_nn_kernel(DecodeArgs d) {
     using G = DecGeom<MT, SC>;
