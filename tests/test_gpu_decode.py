@@ -14,6 +14,8 @@ stay untouched.
                        waves have no block
   17 / 32, 1024, 8192  32-row token tile, 256 slabs of 32, no split
   32, 2048, 1280       32-row token tile, 20 slabs of 64 x 8 K splits
+  16, 256, 1408        44 slabs of 32, no split: two groups of 16 paired
+                       slabs and a tail of 12 in plain order
 """
 import numpy as np
 import pytest
@@ -28,7 +30,7 @@ pytestmark = pytest.mark.gpu
 
 SENTINEL = 12345.0
 CASES = [(16, 8192, 1280), (16, 1024, 8192), (1, 64, 512), (5, 64, 512), (17, 1024, 8192), (32, 1024, 8192),
-         (32, 2048, 1280)]
+         (32, 2048, 1280), (16, 256, 1408)]
 
 
 def _ints(seed, shape, scale=1.0):
