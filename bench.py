@@ -691,12 +691,24 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     res = {}
+    operands = {}
     for name, (M, K, Nn) in shapes.items():
         a = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
         b = torch.randn((K, Nn), device=dev, generator=g).to(torch.bfloat16)
         ms = time_fn(lambda: a @ b, reps)[0]
         res[name] = {"ms": round(ms, 4), "tflops": round(2 * M * K * Nn / (ms * 1e-3) / 1e12, 1)}
+        if name.startswith("attn"):
+            operands[name] = (a, b)
         del a, b
+    # the attention products also as the sequences the library rows time
+    # (forward pair, backward quartet), one product after another
+    seq = {"attn_fwd_sequence": ("attn_qkv", "attn_wo"),
+           "attn_bwd_sequence": ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o")}
+    for name, parts in seq.items():
+        ms = time_fn(lambda: [operands[p][0] @ operands[p][1] for p in parts], reps)[0]
+        fl = sum(2 * shapes[p][0] * shapes[p][1] * shapes[p][2] for p in parts)
+        res[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+    del operands
     log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()
                                                        if not k.startswith("attn")))
     fa = sum(2 * shapes[k][0] * shapes[k][1] * shapes[k][2] for k in ("attn_qkv", "attn_wo"))
@@ -707,7 +719,8 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     res["attn_fwd_total"] = {"ms": round(ta, 4), "tflops": round(fa / (ta * 1e-3) / 1e12, 1)}
     res["attn_bwd_total"] = {"ms": round(tb, 4), "tflops": round(fb / (tb * 1e-3) / 1e12, 1)}
     log(f"[bench] vendor BLAS attention projections: fwd {res['attn_fwd_total']['tflops']}, "
-        f"bwd {res['attn_bwd_total']['tflops']} TFLOP/s")
+        f"bwd {res['attn_bwd_total']['tflops']} TFLOP/s (summed alone); as sequences "
+        f"{res['attn_fwd_sequence']['tflops']}, {res['attn_bwd_sequence']['tflops']}")
     return res
 
 
