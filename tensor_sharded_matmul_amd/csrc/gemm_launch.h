@@ -8,6 +8,7 @@
 
 #include "../../include/tpshard.h"
 #include "gemm_kernel.h"
+#include "mid_tile.h"
 
 namespace tps {
 // Products of one K split whose operand windows are below 2^31 bytes run the
@@ -82,9 +83,6 @@ inline tp_status launch_cfg(const char* fn, const GemmArgs& a, hipStream_t s) {
 // bounds the pitches (elements) so that every offset stays below 2^31.
 static constexpr int64_t kMaxKPitch = (int64_t)1 << 21;
 static constexpr int64_t kMaxMNPitch = (int64_t)1 << 23;
-
-// Compute units of the current device (cached per device; tpshard.hip).
-int device_cus();
 
 // LDS rings per operand layout: K-contiguous operands in stages of 64 k-rows
 // (a tile row is one whole 128-byte line), MN-contiguous ones in 32-row
@@ -206,6 +204,13 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
         // few token rows: 64 x 128 tiles, a smaller ring of the same shape
         using Small = Cfg<64, 128, 64, 128, 64, 3, Rings<A_T, B_KN>::BKB, B_KN ? 4 : 3, 2, 2>;
         if (a.M < 256) return launch_cfg<Small, A_T, B_KN, EPI>(fn, a, s);
+    }
+    if constexpr (MidTile<A_T, B_KN>::kOn && (EPI == EPI_F32 || EPI == EPI_BF16)) {
+        if (a.ksplit == 1 && use_mid_tile<A_T, B_KN, EPI>(a.M, a.N, a.K)) {
+            using MT = MidTile<A_T, B_KN>;
+            using Mid = Cfg<MT::TM, MT::TN, MT::TM, MT::TN, MT::BKA, MT::SA, MT::BKB, MT::SB, MT::WAVES_M, MT::WAVES_N>;
+            return launch_cfg<Mid, A_T, B_KN, EPI>(fn, a, s);
+        }
     }
     // ping-pong forms: 8 waves, 128 x 64 (2 x 4) or 64 x 112 / 112 x 64
     using PSq = CfgPP<A_T, B_KN, 256, 256, 256, 256, 2, 4>;

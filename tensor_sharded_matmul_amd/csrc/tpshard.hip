@@ -15,6 +15,7 @@
 #include "../../include/tpshard.h"
 #include "decode.h"
 #include "gemm_kernel.h"
+#include "mid_tile.h"
 
 namespace tps {
 
@@ -332,6 +333,8 @@ constexpr bool reducible() {
 
 template <bool A_T, bool B_KN, int EPI>
 static SplitPlan plan_of(const GemmArgs& a) {
+    // (a product that runs on mid tiles over its whole K is not split)
+    if (use_mid_tile<A_T, B_KN, EPI>(a.M, a.N, a.K)) return plan_split(a, false, false, false);
     return plan_split(a, EPI == EPI_SWIGLU, !A_T && B_KN, reducible<EPI>());
 }
 

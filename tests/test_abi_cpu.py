@@ -154,7 +154,7 @@ WS_CASES = {
     "tp_row_linear_partial": (16, 8192, 8192),
     "tp_row_linear_partial_chunked": (48, 8192, 8192, 3),
     "tp_mlp_shard_fwd": (16, 8192, 3584, 2),
-    "tp_row_linear_bwd": (4096, 1024, 8192),
+    "tp_row_linear_bwd": (4096, 512, 8192),      # W_O of Llama-3-70B at t = 16
     "tp_vocab_ce_fwd": (4096, 8192, 16128),
     "tp_vocab_embed_bwd": (4096, 16128, 8192),
 }
@@ -194,6 +194,11 @@ def test_workspace_query_values():
     assert T.workspace_size("tp_col_linear", 32, 8192, 1280, 0) > 0
     assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 2 * (16128 // 224) * 12
     assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
+    # the attention shard's dO and dW_O at t = 8 and 4096 tokens run on mid
+    # tiles over the whole K (256 workgroups each): no split; at t = 16
+    # (512 wide) the mid tiles would fill only half of the CUs and dO splits
+    assert T.workspace_size("tp_row_linear_bwd", 4096, 1024, 8192) == 0
+    assert T.workspace_size("tp_row_linear_bwd", 4096, 512, 8192) > 0
     # products with enough output tiles need none
     assert T.workspace_size("tp_mlp_shard_fwd", 4096, 8192, 3584, 2) == 0
     assert T.workspace_size("tp_mlp_shard_bwd", 4096, 8192, 3584, 2) == 0
