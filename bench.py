@@ -84,8 +84,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 1000 steps: the timed region lasts about 1.7 s, long enough for an
+    # outside sampler of GPU activity to see it (20 and 2000 steps gave the
+    # same time per step, within 0.1 %)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=10, help="repetitions per single-kernel timing")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the workload the oracle CPU baseline runs (0 = skip)")
