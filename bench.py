@@ -565,9 +565,6 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
         T.tp_col_linear(X, W_r, "none", Y=Y)
         T.tp_row_linear_partial(O, W_O, P=P)
 
-    ms = time_fn(attn_fwd, reps, warm=8)[0]
-    res["attn_proj_fwd_prefill"] = {"ms": round(ms, 4), "gflop": round(fl_fwd / 1e9, 2),
-                                    "tflops": round(fl_fwd / (ms * 1e-3) / 1e12, 1)}
     dXq = torch.empty((Nq, h), dtype=f32, device=dev)
     dWq = torch.empty((h, width // t), dtype=f32, device=dev)
     dO = torch.empty((Nq, n_h * d_h // t), dtype=bf, device=dev)
@@ -577,9 +574,38 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
         T.tp_col_linear_bwd(X, W_r, dQKV, dX_part=dXq, dW=dWq)
         T.tp_row_linear_bwd(O, W_O, dY, dZ=dO, dW=dWO)
 
-    ms = time_fn(attn_bwd, reps, warm=8)[0]
-    res["attn_proj_bwd_prefill"] = {"ms": round(ms, 4), "gflop": round(2 * fl_fwd / 1e9, 2),
-                                    "tflops": round(2 * fl_fwd / (ms * 1e-3) / 1e12, 1)}
+    # The vendor BLAS (torch.matmul) on the same operands, bf16 outputs, as
+    # plain NN products of contiguous operands (the transposes made here, out
+    # of the timing). Both are timed side by side, three rounds in turn
+    # (medians): the chip's power state carries over from one measurement to
+    # the next, so only measurements taken together compare.
+    W_rT, W_OT, XT, OT = W_r.t().contiguous(), W_O.t().contiguous(), X.t().contiguous(), O.t().contiguous()
+
+    def vendor_fwd():
+        torch.matmul(X, W_r)
+        torch.matmul(O, W_O)
+
+    def vendor_bwd():
+        torch.matmul(dQKV, W_rT)
+        torch.matmul(XT, dQKV)
+        torch.matmul(dY, W_OT)
+        torch.matmul(OT, dY)
+
+    rounds = {k: [] for k in ("fwd", "vendor_fwd", "bwd", "vendor_bwd")}
+    for _ in range(3):
+        for k, fn in (("fwd", attn_fwd), ("vendor_fwd", vendor_fwd), ("bwd", attn_bwd), ("vendor_bwd", vendor_bwd)):
+            rounds[k].append(time_fn(fn, reps, warm=8)[0])
+    for k, fl in (("fwd", fl_fwd), ("bwd", 2 * fl_fwd)):
+        ms, mv = float(np.median(rounds[k])), float(np.median(rounds["vendor_" + k]))
+        res[f"attn_proj_{k}_prefill"] = {
+            "ms": round(ms, 4), "gflop": round(fl / 1e9, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "vendor_blas_ms": round(mv, 4), "vendor_blas_tflops": round(fl / (mv * 1e-3) / 1e12, 1),
+            "rounds_ms": [round(x, 4) for x in rounds[k]],
+            "vendor_rounds_ms": [round(x, 4) for x in rounds["vendor_" + k]]}
+    log(f"[bench] attention prefill, ours vs vendor BLAS side by side: fwd "
+        f"{res['attn_proj_fwd_prefill']['ms']} vs {res['attn_proj_fwd_prefill']['vendor_blas_ms']} ms, bwd "
+        f"{res['attn_proj_bwd_prefill']['ms']} vs {res['attn_proj_bwd_prefill']['vendor_blas_ms']} ms")
+    del W_rT, W_OT, XT, OT
     del dXq, dWq, dO, dWO, Y, P
     # decode, N = 16: weights rotated over 16 copies (> Infinity Cache)
     Wrs = [W_r.clone() for _ in range(16)]
@@ -684,46 +710,20 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
 def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     """Context only: torch.matmul (the ROCm BLAS library) on the step's GEMM
     shapes, bf16 in and out, plain product without the epilogues. Not part of
-    the measured path."""
+    the measured path. (The attention projections are compared with it side
+    by side in their own rows.)"""
     shapes = {"gemm1_gate_up": (N, h, 2 * f), "gemm2_down": (N, f, h), "dx": (N, 2 * f, h),
-              "dw_gate_up": (h, N, 2 * f), "dw_down": (f, N, h),
-              # the Llama-3-70B attention projections of one rank (t = 8), prefill:
-              # QKV and W_O forward, then dX, dW of QKV and dO, dW of W_O
-              "attn_qkv": (N, h, 1280), "attn_wo": (N, 1024, h), "attn_dx_qkv": (N, 1280, h),
-              "attn_dw_qkv": (h, N, 1280), "attn_do": (N, h, 1024), "attn_dw_o": (1024, N, h)}
+              "dw_gate_up": (h, N, 2 * f), "dw_down": (f, N, h)}
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     res = {}
-    operands = {}
     for name, (M, K, Nn) in shapes.items():
         a = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
         b = torch.randn((K, Nn), device=dev, generator=g).to(torch.bfloat16)
         ms = time_fn(lambda: a @ b, reps)[0]
         res[name] = {"ms": round(ms, 4), "tflops": round(2 * M * K * Nn / (ms * 1e-3) / 1e12, 1)}
-        if name.startswith("attn"):
-            operands[name] = (a, b)
         del a, b
-    # the attention products also as the sequences the library rows time
-    # (forward pair, backward quartet), one product after another
-    seq = {"attn_fwd_sequence": ("attn_qkv", "attn_wo"),
-           "attn_bwd_sequence": ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o")}
-    for name, parts in seq.items():
-        ms = time_fn(lambda: [operands[p][0] @ operands[p][1] for p in parts], reps)[0]
-        fl = sum(2 * shapes[p][0] * shapes[p][1] * shapes[p][2] for p in parts)
-        res[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
-    del operands
-    log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()
-                                                       if not k.startswith("attn")))
-    fa = sum(2 * shapes[k][0] * shapes[k][1] * shapes[k][2] for k in ("attn_qkv", "attn_wo"))
-    fb = sum(2 * shapes[k][0] * shapes[k][1] * shapes[k][2]
-             for k in ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o"))
-    ta = sum(res[k]["ms"] for k in ("attn_qkv", "attn_wo"))
-    tb = sum(res[k]["ms"] for k in ("attn_dx_qkv", "attn_dw_qkv", "attn_do", "attn_dw_o"))
-    res["attn_fwd_total"] = {"ms": round(ta, 4), "tflops": round(fa / (ta * 1e-3) / 1e12, 1)}
-    res["attn_bwd_total"] = {"ms": round(tb, 4), "tflops": round(fb / (tb * 1e-3) / 1e12, 1)}
-    log(f"[bench] vendor BLAS attention projections: fwd {res['attn_fwd_total']['tflops']}, "
-        f"bwd {res['attn_bwd_total']['tflops']} TFLOP/s (summed alone); as sequences "
-        f"{res['attn_fwd_sequence']['tflops']}, {res['attn_bwd_sequence']['tflops']}")
+    log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()))
     return res
 
 

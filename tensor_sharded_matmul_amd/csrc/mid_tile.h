@@ -9,27 +9,24 @@ namespace tps {
 // Compute units of the current device (cached per device; tpshard.hip).
 int device_cus();
 
-// Mid tiles: 128 token rows by 128 (NT) or 256 (TN) columns. A product
-// with a plain epilogue whose 256 x 256 tiles would leave at least half of
-// the CUs idle, but whose mid tiles fill more than half of them in one wave,
-// runs mid tiles over its whole K instead of a K split: no fp32 partials and
-// no reduction launch. On the attention shards of Llama-3-70B at t = 8 and
-// 4096 tokens these are dO = dY W_O^T (NT, 1024 wide: 74 -> 63 us) and
-// dW_O = O^T dY (TN, 1024 x 8192: 78 -> 65 us). The NN products keep their
-// K split: the 1280-wide QKV forward on 128 x 160 tiles (from 256 loaded
-// columns) took as long as its split and reduction alone, and longer in the
-// forward sequence.
+// Mid tiles: 128 x 256 tiles for the weight gradients (TN). A TN product
+// with a plain epilogue (fp32 or bf16) whose 256 x 256 tiles would leave at
+// least half of the CUs idle, but whose mid tiles fill more than half of
+// them in one wave, runs mid tiles over its whole K instead of a K split: no
+// fp32 partials, no reduction launch. On the attention shard of
+// Llama-3-70B at t = 8 and 4096 tokens this is dW_O = O^T dY (1024 x 8192):
+// 66 us in the backward sequence against 62 us for 2 splits plus 17 us for
+// their reduction. The same rule on the NT and NN layouts (dO on 128 x 128
+// tiles, the QKV forward on 128 x 160 tiles) ran faster alone but slower
+// inside the sequences of products, where the chip sits at its power limit
+// and a small tile's extra operand traffic costs clock: those keep the
+// split.
 template <bool A_T, bool B_KN>
 struct MidTile {
     static constexpr bool kOn = false;
 };
 template <>
-struct MidTile<false, false> {  // NT: 4 waves of 64 x 64, both rings 4 x 16 KB
-    static constexpr bool kOn = true;
-    static constexpr int TM = 128, TN = 128, BKA = 64, SA = 4, BKB = 64, SB = 4, WAVES_M = 2, WAVES_N = 2;
-};
-template <>
-struct MidTile<true, true> {  // TN: 8 waves of 64 x 64, rings of 6 x 8 KB and 6 x 16 KB
+struct MidTile<true, true> {  // 8 waves of 64 x 64, rings of 6 x 8 KB (A) and 6 x 16 KB (B)
     static constexpr bool kOn = true;
     static constexpr int TM = 128, TN = 256, BKA = 32, SA = 6, BKB = 32, SB = 6, WAVES_M = 2, WAVES_N = 4;
 };

@@ -194,11 +194,12 @@ def test_workspace_query_values():
     assert T.workspace_size("tp_col_linear", 32, 8192, 1280, 0) > 0
     assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 2 * (16128 // 224) * 12
     assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
-    # the attention shard's dO and dW_O at t = 8 and 4096 tokens run on mid
-    # tiles over the whole K (256 workgroups each): no split; at t = 16
-    # (512 wide) the mid tiles would fill only half of the CUs and dO splits
-    assert T.workspace_size("tp_row_linear_bwd", 4096, 1024, 8192) == 0
-    assert T.workspace_size("tp_row_linear_bwd", 4096, 512, 8192) > 0
+    # a weight gradient on TN mid tiles (2112 x 1984 over 3000 tokens: 136
+    # tiles of 128 x 256, 72 of 256 x 256) is not split, and dZ of the same
+    # call contracts over K = 1984 < 2048 without a split: no workspace
+    assert T.workspace_size("tp_row_linear_bwd", 3000, 2112, 1984) == 0
+    # dO of the attention shard at 4096 tokens splits (64 large tiles)
+    assert T.workspace_size("tp_row_linear_bwd", 4096, 1024, 8192) > 0
     # products with enough output tiles need none
     assert T.workspace_size("tp_mlp_shard_fwd", 4096, 8192, 3584, 2) == 0
     assert T.workspace_size("tp_mlp_shard_bwd", 4096, 8192, 3584, 2) == 0

@@ -20,8 +20,8 @@ keeps the oracle fast:
   TN 224x256, fp32 store (dW_down)     Z^T dY   3584 x 8192, 300 tokens      512
 
 and the attention projections run at their own sizes (below), which also
-select the mid tiles (NT 128 x 128 for dO, TN 128 x 256 for dW_O); a ragged
-case covers those two tiles on every edge.
+select the TN 128 x 256 mid tile (dW_O); a ragged case covers that tile on
+every edge.
 
 Integer-valued inputs (small integers, times a power of two where an
 activation should see values of order one) make every product exact in f32
@@ -163,9 +163,9 @@ def test_dw_down_tn_224x256_fp32():
 
 # The attention projections of one Llama-3-70B rank at t = 8 (h = 8192,
 # W_r 1280 wide, W_O 1024 rows), prefill N = 4096 and decode N = 16, every
-# product of the forward and backward: split-K (the QKV forward at 4096 and
-# 16 tokens), the decode kernel (both forward products at 16), mid tiles
-# (dO and dW of W_O at 4096) and the large tiles.
+# product of the forward and backward: split-K (the QKV forward and dO at
+# 4096 tokens, dO and dW_O at 16), the decode kernel (both forward products
+# at 16), the TN mid tile (dW_O at 4096) and the large tiles.
 @pytest.mark.parametrize("N", [4096, 16])
 def test_attention_projection_products_exact(N):
     h, wq, wo = 8192, 1280, 1024
@@ -189,30 +189,22 @@ def test_attention_projection_products_exact(N):
     assert np.array_equal(f64(dWO), Oa.T @ dY)
 
 
-# Mid tiles: products whose 256 x 256 tiles would fill at most half of the
-# 256 CUs but whose 128-row tiles fill more than half, with K >= 2048, run
-# one wave of mid tiles over the whole K (no split, no workspace). Ragged on
-# every edge: 3000 tokens (23.4 tiles of 128 rows; the TN contraction, not a
-# multiple of 32), 960 shard columns (7.5 tiles of 128), 4160 model columns
-# (16.25 tiles of 256).
-def test_mid_tiles_nt_tn_ragged_exact():
-    N, k_loc, n = 3000, 960, 4160
+# The TN mid tile (128 x 256): a weight gradient whose 256 x 256 tiles would
+# fill at most half of the 256 CUs but whose mid tiles fill more than half,
+# with K >= 2048 tokens, runs one wave of mid tiles over the whole K (no
+# split, no workspace). Ragged on every edge: 2112 weight rows (16.5 tiles
+# of 128), 1984 columns (7.75 tiles of 256), 3000 tokens (not a multiple of
+# 32). dZ of the same call (K = 1984) takes the large tiles without a split.
+def test_mid_tile_tn_ragged_exact():
+    N, k_loc, n = 3000, 2112, 1984
     assert T.workspace_size("tp_row_linear_bwd", N, k_loc, n) == 0
     Zb, Z = _ints(240, (N, k_loc))
     Wb, W = _ints(241, (k_loc, n))
     dYb, dY = _ints(242, (N, n))
     bz, dZ = _canary((N, k_loc), torch.bfloat16)
     bw, dW = _canary((k_loc, n), torch.float32)
-    T.tp_row_linear_bwd(to_dev(Zb), to_dev(Wb), to_dev(dYb), dZ=dZ, dW=dW)   # NT bf16, TN fp32
-    # the NT tile with an fp32 store: dX_part = dQ W^T of a column-parallel layer
-    n2 = 2112
-    Wcb, Wc = _ints(243, (k_loc, n2))
-    dQb, dQ = _ints(244, (N, n2))
-    bx, dX = _canary((N, k_loc), torch.float32)
-    Xd = torch.empty((N, k_loc), dtype=torch.bfloat16, device="cuda:0")
-    T.tp_col_linear_bwd(Xd, to_dev(Wcb), to_dev(dQb), dX_part=dX, want_dw=False)
+    T.tp_row_linear_bwd(to_dev(Zb), to_dev(Wb), to_dev(dYb), dZ=dZ, dW=dW)
     torch.cuda.synchronize()
-    assert np.array_equal(bits(dZ), rne_bf16_bits(dY @ W.T))
     assert np.array_equal(f64(dW), Z.T @ dY)
-    assert np.array_equal(f64(dX), dQ @ Wc.T)
-    assert _untouched(bz, N * k_loc) and _untouched(bw, k_loc * n) and _untouched(bx, N * k_loc)
+    assert np.array_equal(bits(dZ), rne_bf16_bits(dY @ W.T))
+    assert _untouched(bz, N * k_loc) and _untouched(bw, k_loc * n)
