@@ -51,13 +51,13 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 
 
 def kernel_sources_sha() -> str:
-    """Hash of the library's kernel sources (not the MFMA rate probe beside
+    """Hash of the library's kernel sources (not the stand-alone probes beside
     them), to tell whether recorded counters are current."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip")) and f != "mfma_rate.hip":
+        if f.endswith((".h", ".hip")) and f not in ("mfma_rate.hip", "store_rate.hip"):
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -105,6 +105,8 @@ def parse():
     ap.add_argument("--attn-prefill-only", type=int, default=0, metavar="CALLS",
                     help="only run the six attention-projection products of one Llama-3-70B rank at 4096 "
                          "tokens (and the vendor BLAS on the same products) CALLS times (for profiling), then exit")
+    ap.add_argument("--store-rate", action="store_true",
+                    help="only run the store-throughput probe (one CU's fp32 / bf16 stores) and print its records")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="only run the MFMA rate probe (bf16 16x16x32 MFMAs on register operands, no memory "
                          "traffic; random and all-zero data) and print its JSON lines, then exit")
@@ -131,6 +133,10 @@ def main() -> int:
         return 1
     if args.mfma_rate:
         for r in mfma_rate():
+            print(json.dumps(r), flush=True)
+        return 0
+    if args.store_rate:
+        for r in run_probe("store_rate"):
             print(json.dumps(r), flush=True)
         return 0
     T.load()
@@ -452,6 +458,19 @@ def main() -> int:
         if clk:
             rows["mfma_rate_no_memory"]["device_max_sclk_mhz"] = clk["max_sclk_mhz"]
         log(f"[bench] MFMA rate without memory traffic: {rows['mfma_rate_no_memory']}")
+        # one CU's store throughput: what a GEMM tile's epilogue costs
+        sr = [r for r in run_probe("store_rate") if "pattern" in r]
+        pick = lambda pat, w, n: next(r for r in sr if r["pattern"] == pat and r["waves"] == w and r["workgroups"] == n)  # noqa: E731
+        rows["store_rate_per_cu"] = {
+            "fp32_epilogue_gbs_per_cu": {f"{n}_cus_{w}_waves": pick("epilogue_fp32", w, n)["gbs_per_workgroup"]
+                                         for n in (32, 256) for w in (4, 8, 16)},
+            "fp32_mfma_layout_gbs_per_cu": {f"{n}_cus": pick("mfma_layout_fp32", 8, n)["gbs_per_workgroup"] for n in (32, 256)},
+            "fp32_rows_gbs_per_cu_256": pick("rows_fp32", 8, 256)["gbs_per_workgroup"],
+            "bf16_epilogue_gbs_per_cu_256": pick("epilogue_bf16", 8, 256)["gbs_per_workgroup"],
+            "us_per_256x256_fp32_tile_all_cus": {
+                "swapped": round(262144 / (pick("epilogue_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2),
+                "mfma_layout": round(262144 / (pick("mfma_layout_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2)}}
+        log(f"[bench] store rate per CU: {rows['store_rate_per_cu']}")
 
     # ---------------- CPU baseline: the oracle on a token sample ----------------
     cpu = None
@@ -727,17 +746,23 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
     return res
 
 
-def mfma_rate(iters=20000, reps=3):
-    """Run the MFMA rate probe built beside the library (a child process on
-    the same GPU); returns its records {data, rep, ms, tflops}."""
+def run_probe(name, *args):
+    """Run a stand-alone probe built beside the library (a child process on
+    the same GPU); returns its JSON records."""
     import subprocess
-    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", "mfma_rate")
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tensor_sharded_matmul_amd", name)
     if not os.path.exists(exe):
         raise RuntimeError(f"{exe} is not built; run `python -m tensor_sharded_matmul_amd.build`")
-    r = subprocess.run([exe, str(iters), str(reps)], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=120)
     if r.returncode != 0:
-        raise RuntimeError(f"mfma_rate failed ({r.returncode}): {r.stderr.strip()[-500:]}")
+        raise RuntimeError(f"{name} failed ({r.returncode}): {r.stderr.strip()[-500:]}")
     return [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+
+
+def mfma_rate(iters=20000, reps=3):
+    """The MFMA rate probe's records {data, rep, ms, tflops} (and the device
+    header)."""
+    return run_probe("mfma_rate", iters, reps)
 
 
 def device_clock(records):

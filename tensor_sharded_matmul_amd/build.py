@@ -17,7 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpshard.so")
 # the MFMA rate probe (bench.py --mfma-rate): a standalone executable
-PROBE_SRC, PROBE = "mfma_rate.hip", os.path.join(HERE, "mfma_rate")
+# stand-alone probes built beside the library: the MFMA rate with no memory
+# traffic, and one CU's store throughput
+PROBES = [("mfma_rate.hip", os.path.join(HERE, "mfma_rate")), ("store_rate.hip", os.path.join(HERE, "store_rate"))]
 SOURCES = ["tpshard.hip", "gemm_nn_store.hip", "gemm_nn_act.hip", "gemm_nn_ce.hip", "gemm_nt_store.hip",
            "gemm_nt_act.hip", "gemm_tn.hip", "gemm_decode.hip"]
 ARCH = "gfx950"
@@ -102,11 +104,12 @@ def build(asm_dir: str | None = None, verbose: bool = True) -> str:
         print("[build]", " ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    cmd = [hipcc()] + flags() + [os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
-    if verbose:
-        print("[build]", " ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(PROBE + ".tmp", PROBE)
+    for src, exe in PROBES:
+        cmd = [hipcc()] + flags() + [os.path.join(CSRC, src), "-o", exe + ".tmp"]
+        if verbose:
+            print("[build]", " ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 

@@ -13,9 +13,12 @@
 //  * WAVES_M x WAVES_N waves of 64 lanes (4, or 8 = two per SIMD), one
 //    workgroup per CU. Each wave owns a (TM/WAVES_M) x (TN/WAVES_N) sub-tile
 //    of C in f32 accumulators (AGPRs).
-//  * v_mfma_f32_16x16x32_bf16 with the operands swapped (the MFMA "A" operand
-//    is the B tile), so each lane ends with 4 consecutive columns of one C row
-//    and epilogue stores are 16-byte (f32) or 8-byte (bf16) vectors.
+//  * v_mfma_f32_16x16x32_bf16. For the bf16 and fused epilogues the operands
+//    are swapped (the MFMA "A" operand is the B tile), so each lane ends with
+//    4 consecutive columns of one C row (8-byte bf16 stores, per-row
+//    reductions within a lane). fp32 outputs keep the MFMA's own layout (a
+//    lane holds one column of 4 rows): 16 consecutive lanes then store 64
+//    contiguous bytes, which the CU's store path takes at 64 B per clock.
 //  * Operand tiles go HBM -> LDS directly (buffer_load_dwordx4 ... lds: no
 //    staging registers) into a ring of STAGES buffers of BK k-rows. A stage
 //    is refilled as soon as its MFMA fragments are in registers, so STAGES-1
@@ -77,6 +80,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kGroupM = 4;     // tile rows per L2 group
+#ifndef TPS_F32_COLS
+#define TPS_F32_COLS 1         // fp32 outputs stored from the MFMA's own layout
+#endif
 
 enum Epi : int {
     EPI_F32 = 0,        // C f32 = acc (or += acc)
@@ -681,6 +687,78 @@ __device__ __forceinline__ void epilogue_f32_store_acc(const f32x4_t (&acc)[MI][
     });
 }
 
+// fp32 stores from the MFMA's own accumulator layout: lane l holds column
+// l % 16 of rows 4 (l / 16) + r, r = 0..3, of each 16 x 16 block. A store of
+// register r then writes 64 contiguous bytes from each 16 lanes (4 rows of
+// the block): the CU's store path takes 64 bytes of consecutive lanes per
+// clock, against one lane (16 bytes) per clock when consecutive lanes write
+// different rows, as the 16-byte stores of the swapped layout do (measured
+// with the store-rate probe: 95 against 38 GB/s per CU, 54 against 37 GB/s
+// with all 256 CUs storing).
+// Each value leaves its AGPR through inline asm (a store, or a read into a
+// VGPR to add it to C): written as plain C++, the compiler copies the whole
+// accumulator array to VGPRs first and spills.
+// (the 16-column blocks of a row differ by a constant, folded into the
+// instruction's offset: one address per row)
+template <int OFF>
+__device__ __forceinline__ void store_f32_acc(float* p, float v) {
+    asm volatile("global_store_dword %0, %1, off offset:%2" ::"v"(p), "a"(v), "i"(OFF) : "memory");
+}
+
+__device__ __forceinline__ float read_acc(float v) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v));
+    return x;
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_f32_cols(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,
+                                                  int nb) {
+    auto rows = [&](auto accc) {
+        constexpr bool ACC = decltype(accc)::value;
+        static_for<0, MI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<0, 4>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                const int m = mb + i * 16 + r;
+                if (m < args.M) {
+                    float* row = reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb;
+                    static_for<0, NI>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        if (nb + j * 16 < args.N) {
+                            if constexpr (ACC) row[j * 16] += read_acc(acc[i][j][r]);
+                            else store_f32_acc<j * 64>(row, acc[i][j][r]);
+                        }
+                    });
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    if (args.accumulate) rows(std::true_type{});
+    else rows(std::false_type{});
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void epilogue_f32_cols_store_acc(const f32x4_t (&acc)[MI][NI], const GemmArgs& args,
+                                                            int mb, int nb) {
+    static_for<0, MI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const int m = mb + i * 16 + r;
+            if (m < args.M) {
+                float* row = reinterpret_cast<float*>(args.C) + (size_t)m * args.ldc + nb;
+                static_for<0, NI>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    if (nb + j * 16 < args.N) store_f32_acc<j * 64>(row, acc[i][j][r]);
+                });
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 // ---------------------------------------------------------------------------
 // Tile configuration.
 //   BM x BN   loaded operand tiles (LDS); TM x TN computed tile (TM <= BM,
@@ -767,6 +845,9 @@ gemm_kernel(const GemmArgs args) {
     constexpr int NWAVES = WAVES_M * WAVES_N;
     constexpr bool SWIGLU = (EPI == EPI_SWIGLU);
     constexpr bool GATEUP = SWIGLU;                  // B tile = [gate | up] halves
+    // fp32 outputs: accumulators in the MFMA's own layout (a lane holds one
+    // column of 4 rows), stored a row of 16 consecutive floats per 16 lanes
+    constexpr bool COLS = (EPI == EPI_F32) && TPS_F32_COLS != 0;
     constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
     constexpr int MI = WM / 16, NI = WN / 16;
     constexpr int PA = BKA / 32, PB = BKB / 32;     // k32 sub-steps per stage
@@ -928,7 +1009,10 @@ gemm_kernel(const GemmArgs args) {
     auto mfma_one = [&acc](const Frags& fr, auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int i = m / NI, j = m % NI;
-        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fr.b[j]), "v"(fr.a[i]));
+        if constexpr (COLS)
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fr.a[i]), "v"(fr.b[j]));
+        else
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fr.b[j]), "v"(fr.a[i]));
     };
     // (decode tiles, at most 32 token rows, stream the weight and are bound
     // by HBM, not by the MFMA issue; they may load more often than they MFMA)
@@ -1242,17 +1326,21 @@ gemm_kernel(const GemmArgs args) {
     }
 
     const int lr = lane & 15, lq = lane >> 4;
-    const int mb = m0 + wm * WM + lr;
-    const int nb = n0 + wn * (SWIGLU ? WN / 2 : WN) + lq * 4;
+    // the lane's first output row and column: row l % 16 and 4 columns from
+    // 4 (l / 16) (operands swapped), or column l % 16 and 4 rows (COLS)
+    const int mb = m0 + wm * WM + (COLS ? 4 * lq : lr);
+    const int nb = n0 + wn * (SWIGLU ? WN / 2 : WN) + (COLS ? lr : 4 * lq);
     if constexpr (EPI == EPI_F32 && !PP) {  // split-K partials are plain fp32 stores
         GemmArgs part = args;
         if (args.ksplit > 1) {
             part.C = reinterpret_cast<float*>(args.C) + (size_t)split * args.M * args.ldc;
             part.accumulate = 0;
         }
-        epilogue<MI, NI, EPI_F32>(acc, part, mb, nb);
+        if constexpr (COLS) epilogue_f32_cols<MI, NI>(acc, part, mb, nb);
+        else epilogue<MI, NI, EPI_F32>(acc, part, mb, nb);
     } else if constexpr (EPI == EPI_F32) {  // ping-pong: one K split, C overwritten
-        epilogue_f32_store_acc<MI, NI>(acc, args, mb, nb);
+        if constexpr (COLS) epilogue_f32_cols_store_acc<MI, NI>(acc, args, mb, nb);
+        else epilogue_f32_store_acc<MI, NI>(acc, args, mb, nb);
     } else {
         epilogue<MI, NI, EPI>(acc, args, mb, nb);
     }
