@@ -296,8 +296,10 @@ tp_status tp_kv_grad_accumulate(float* dW_dst, const float* dW_src, int64_t h,
  *   m_i, s_i, zy_i f32 [N]: per token the local max of z, sum of
  *   exp(z - m_i) over the rank's range, and z of the target when the target
  *   is in the range (0 otherwise).
- * Its workspace holds per-tile records: N * 2 * ceil(v_loc / 224) * 12
- * bytes.
+ * Its workspace holds per-tile records, 12 bytes per token and 64-column
+ * block: N * 4 * ceil(v_loc / 256) * 12 bytes; when (h + 512) * v_loc * 2
+ * reaches 2^31 (a weight window past 32-bit offsets), one per 112-column
+ * block: N * 2 * ceil(v_loc / 224) * 12 bytes.
  */
 tp_status tp_vocab_ce_fwd_workspace_size(int64_t N, int64_t h, int64_t v_loc,
                                          size_t* bytes);

@@ -120,9 +120,21 @@ struct GemmArgs {
     int col0;
 };
 
-// Output columns per tile of the cross-entropy statistics GEMM (2 waves of
-// 112 columns each write one record per row).
-constexpr int kCeTileN = 224;
+// The cross-entropy statistics GEMM writes one record per row for each
+// wave column block of its tiles. It runs the ping-pong 256 x 256 tile (4
+// wave column blocks of 64 columns) unless the weight's window reaches 2^31
+// bytes (the WIDE variant, which the ping-pong kernel does not have): then
+// 256 x 224 tiles of 2 x 2 waves (2 blocks of 112 columns). K = h, the
+// weight's pitch ldb = v_loc.
+#ifndef TPS_CE_PP
+#define TPS_CE_PP 1
+#endif
+inline bool ce_stats_pingpong(int64_t K, int64_t ldb) {
+    return TPS_CE_PP != 0 && (K + 512) * ldb * 2 < ((int64_t)1 << 31);
+}
+inline int ce_parts(int64_t K, int64_t v_loc) {
+    return ce_stats_pingpong(K, v_loc) ? (int)(4 * ((v_loc + 255) / 256)) : (int)(2 * ((v_loc + 223) / 224));
+}
 
 // Token rows of the tile a split-K product of M rows runs with.
 inline int splitk_tile_m(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
@@ -481,6 +493,14 @@ __device__ __forceinline__ void epilogue_act_bwd(const f32x4_t (&acc)[MI][NI], c
     });
 }
 
+// One accumulator read from its AGPR into a VGPR (inline asm: as plain C++
+// the compiler may copy a whole accumulator array to VGPRs first).
+__device__ __forceinline__ float read_acc(float v) {
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v));
+    return x;
+}
+
 // Vocab-parallel cross-entropy, forward: the logits never leave registers.
 // For each row, the 4 lanes that hold it (lane, lane ^ 16, lane ^ 32,
 // lane ^ 48) reduce this wave's 16 NI columns to the record
@@ -509,7 +529,8 @@ __device__ __forceinline__ void epilogue_ce_stats(const f32x4_t (&acc)[MI][NI], 
         float run_m = -__builtin_inff(), run_s = 0.f, zy = 0.f;
         static_for<0, NI>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            const f32x4_t v = acc[i][j];
+            float v[4];
+            static_for<0, 4>([&](auto rc) { v[decltype(rc)::value] = read_acc(acc[i][j][decltype(rc)::value]); });
             float gm = -__builtin_inff();
             static_for<0, 4>([&](auto rc) {
                 constexpr int r = decltype(rc)::value;
@@ -695,7 +716,7 @@ __device__ __forceinline__ void epilogue_f32_store_acc(const f32x4_t (&acc)[MI][
 // different rows, as the 16-byte stores of the swapped layout do (measured
 // with the store-rate probe: 95 against 38 GB/s per CU, 54 against 37 GB/s
 // with all 256 CUs storing).
-// Each value leaves its AGPR through inline asm (a store, or a read into a
+// Each value leaves its AGPR through inline asm (a store, or read_acc into a
 // VGPR to add it to C): written as plain C++, the compiler copies the whole
 // accumulator array to VGPRs first and spills.
 // (the 16-column blocks of a row differ by a constant, folded into the
@@ -705,11 +726,6 @@ __device__ __forceinline__ void store_f32_acc(float* p, float v) {
     asm volatile("global_store_dword %0, %1, off offset:%2" ::"v"(p), "a"(v), "i"(OFF) : "memory");
 }
 
-__device__ __forceinline__ float read_acc(float v) {
-    float x;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v));
-    return x;
-}
 
 template <int MI, int NI>
 __device__ __forceinline__ void epilogue_f32_cols(const f32x4_t (&acc)[MI][NI], const GemmArgs& args, int mb,

@@ -245,11 +245,15 @@ tp_status launch_gemm(const char* fn, GemmArgs a, hipStream_t s) {
     a.a_bytes = (uint64_t)(A_T ? a.K : a.M) * (uint64_t)a.lda * 2u;
     a.b_bytes = (uint64_t)(B_KN ? a.K : a.N) * (uint64_t)a.ldb * 2u;
     if constexpr (EPI == EPI_CE_STATS) {
+        // one record per row for each wave column block: the host sizes its
+        // record buffer for the shape ce_parts names (the interleaved
+        // 256 x 256 tile of 4 waves would spill a register)
+        static_assert(!A_T && B_KN, "the statistics GEMM is a forward (NN) product");
+        if (ce_stats_pingpong(a.K, a.ldb)) {
+            using PSq = CfgPP<A_T, B_KN, 256, 256, 256, 256, 2, 4>;
+            return launch_cfg<PSq, A_T, B_KN, EPI>(fn, a, s);
+        }
         using N224 = CfgOf<A_T, B_KN, 256, 256, 256, 224, 2, 2>;
-        // one record per row for each 112-column wave block of 256 x 224
-        // tiles (kCeTileN; the 256 x 256 tile would spill a register): the
-        // host sizes its record buffer for exactly this shape
-        static_assert(N224::TN == kCeTileN, "record layout");
         return launch_cfg<N224, A_T, B_KN, EPI>(fn, a, s);
     } else {
         return launch_by_shape<A_T, B_KN, EPI>(fn, a, s);

@@ -872,10 +872,11 @@ static tp_status check_targets(const char* fn, int64_t N, const int32_t* targets
     return TP_OK;
 }
 
-// records: 2 wave column blocks per kCeTileN-wide tile (launch_gemm runs
-// EPI_CE_STATS with 256 x 224 tiles of 2 x 2 waves), 3 floats each per row
-static int ce_parts(int64_t v_loc) { return (int)(2 * ((v_loc + kCeTileN - 1) / kCeTileN)); }
-static size_t ce_fwd_need(int64_t N, int64_t v_loc) { return (size_t)N * ce_parts(v_loc) * 3 * sizeof(float); }
+// records: one per row and wave column block of the statistics GEMM's tiles
+// (ce_parts), 3 floats each
+static size_t ce_fwd_need(int64_t N, int64_t h, int64_t v_loc) {
+    return (size_t)N * ce_parts(h, v_loc) * 3 * sizeof(float);
+}
 
 static void ce_bwd_args(const void* X, const void* W_i, void* dZ, float* dX_part, float* dW_i, int64_t N, int64_t h,
                         int64_t v_loc, int accumulate, GemmArgs& b, GemmArgs& c) {
@@ -1236,7 +1237,7 @@ tp_status tp_vocab_ce_fwd_workspace_size(int64_t N, int64_t h, int64_t v_loc, si
     const char* fn = "tp_vocab_ce_fwd_workspace_size";
     TP_QUERY_OUT(bytes);
     TP_TRY(check_ce(fn, N, h, v_loc, 0));
-    *bytes = ce_fwd_need(N, v_loc);
+    *bytes = ce_fwd_need(N, h, v_loc);
     return ok();
 }
 
@@ -1251,10 +1252,10 @@ tp_status tp_vocab_ce_fwd(const void* X, const void* W_i, const int32_t* targets
     TP_CHECK_TOK_PTR(m_i, "m_i");
     TP_CHECK_TOK_PTR(s_i, "s_i");
     TP_CHECK_TOK_PTR(zy_i, "zy_i");
-    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, ce_fwd_need(N, v_loc)));
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, ce_fwd_need(N, h, v_loc)));
     if (N == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int nparts = ce_parts(v_loc);
+    const int nparts = ce_parts(h, v_loc);
     float* rec = static_cast<float*>(workspace);
     GemmArgs a = make_args(X, W_i, rec, (int)N, (int)v_loc, (int)h, (int)h, (int)v_loc, nparts);
     a.tgt = targets;

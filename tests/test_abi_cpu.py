@@ -177,8 +177,10 @@ def test_workspace_queries(entry):
 
 def test_workspace_query_values():
     # the split-K decode product: ksplit partials of [N, n] f32; the
-    # cross-entropy records: 2 per 224 vocab columns per token, 12 bytes
-    # each; the embedding stamps: 4 bytes per table row
+    # cross-entropy records: one per 64 vocab columns per token (256 x 256
+    # ping-pong tiles), or one per 112 when the weight's window needs 64-bit
+    # offsets (256 x 224 tiles), 12 bytes each; the embedding stamps: 4 bytes
+    # per table row
     n = T.workspace_size("tp_col_linear", 16, 8192, 1280, 0)
     assert n % (16 * 1280 * 4) == 0 and 2 <= n // (16 * 1280 * 4) <= 64
     # decode plans (256 CUs): 32-column slabs when no K split is needed (at
@@ -192,7 +194,10 @@ def test_workspace_query_values():
     assert T.workspace_size("tp_col_linear", 16, 256, 4096, 2) == 0   # SwiGLU, 8192 weight columns: no split
     assert T.workspace_size("tp_col_linear", 32, 2048, 1280, 0) == 8 * 32 * 1280 * 4
     assert T.workspace_size("tp_col_linear", 32, 8192, 1280, 0) > 0
-    assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 2 * (16128 // 224) * 12
+    assert T.workspace_size("tp_vocab_ce_fwd", 4096, 8192, 16128) == 4096 * 4 * (16128 // 256) * 12
+    # (8192 + 512) * 131072 * 2 >= 2^31: a 131072-wide vocabulary shard
+    assert T.workspace_size("tp_vocab_ce_fwd", 64, 8192, 131072) == 64 * 2 * -(-131072 // 224) * 12
+    assert T.workspace_size("tp_vocab_ce_fwd", 64, 8192, 123200) == 64 * 4 * -(-123200 // 256) * 12
     assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
     # a weight gradient on TN mid tiles (2112 x 1984 over 3000 tokens: 136
     # tiles of 128 x 256, 72 of 256 x 256) is not split, and dZ of the same
