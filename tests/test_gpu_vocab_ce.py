@@ -65,6 +65,26 @@ def test_vocab_ce_forward_backward_small(N, h, v_loc, t):
     assert err(f64(dX), want_dx) <= TOL
 
 
+def test_vocab_ce_forward_wide_weight_window():
+    # a vocabulary shard so wide that the weight's window ((h + 512) rows of
+    # its pitch) reaches 2^31 bytes: the statistics GEMM then runs 256 x 224
+    # tiles with the WIDE descriptor walk (one record per 112 columns). The
+    # widest shard the library takes (2^20 columns) over h = 512.
+    N, h, v_loc = 16, 512, 1 << 20
+    assert (h + 512) * v_loc * 2 >= 1 << 31
+    assert T.workspace_size("tp_vocab_ce_fwd", N, h, v_loc) == N * 2 * -(-v_loc // 224) * 12
+    rng = np.random.default_rng(4242)
+    X = synth.draw(rng, (N, h))
+    W = synth.draw(rng, (h, v_loc), fan_in=h)
+    y = rng.integers(0, v_loc, size=N).astype(np.int32)
+    y[:3] = [0, v_loc - 1, v_loc // 2]
+    print(f"ce wide window: N={N} h={h} v_loc={v_loc}", flush=True)
+    m_i, s_i, zy_i = T.tp_vocab_ce_fwd(to_dev(X), to_dev(W), _dev_i32(y), 0)
+    torch.cuda.synchronize()
+    wm, ws, wz = O.vocab_ce_local(synth.bf16_to_f64(X), synth.bf16_to_f64(W), y, 0)
+    assert err(f64(m_i), wm) <= TOL and err(f64(s_i), ws) <= TOL and err(f64(zy_i), wz) <= TOL
+
+
 def _rows(n, k, seed):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=k, replace=False)]))
