@@ -80,6 +80,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int kGroupM = 4;     // tile rows per L2 group
+#ifndef TPS_PP_SPLIT
+#define TPS_PP_SPLIT 1         // split-K partials of forward (NN) products on the ping-pong kernel
+#endif
 #ifndef TPS_F32_COLS
 #define TPS_F32_COLS 1         // fp32 outputs stored from the MFMA's own layout
 #endif
@@ -1354,9 +1357,12 @@ gemm_kernel(const GemmArgs args) {
         }
         if constexpr (COLS) epilogue_f32_cols<MI, NI>(acc, part, mb, nb);
         else epilogue<MI, NI, EPI_F32>(acc, part, mb, nb);
-    } else if constexpr (EPI == EPI_F32) {  // ping-pong: one K split, C overwritten
-        if constexpr (COLS) epilogue_f32_cols_store_acc<MI, NI>(acc, args, mb, nb);
-        else epilogue_f32_store_acc<MI, NI>(acc, args, mb, nb);
+    } else if constexpr (EPI == EPI_F32) {  // ping-pong: C (or split s's partial) overwritten
+        GemmArgs part = args;
+        if (TPS_PP_SPLIT != 0 && args.ksplit > 1)
+            part.C = reinterpret_cast<float*>(args.C) + (size_t)split * args.M * args.ldc;
+        if constexpr (COLS) epilogue_f32_cols_store_acc<MI, NI>(acc, part, mb, nb);
+        else epilogue_f32_store_acc<MI, NI>(acc, part, mb, nb);
     } else {
         epilogue<MI, NI, EPI>(acc, args, mb, nb);
     }
