@@ -443,39 +443,38 @@ def main() -> int:
     rows["bwd_tflops"] = round(bwd_flops / (rows["bwd_ms"] * 1e-3) / 1e12, 1)
 
     del Z, H, P, dH, dX, dWi, dWo
+    # The context rows below are measured after the step: a Python-level
+    # failure in one of them (an error a call returns, a probe that cannot
+    # run) is recorded under rows["errors"] and the line is still printed.
+    errors = {}
+
+    def guarded(name, fn):
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001
+            import traceback
+            traceback.print_exc(file=sys.stderr)
+            errors[name] = f"{type(e).__name__}: {e}"[:400]
+            return None
+
     if not args.no_rows:
-        rows.update(measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, args.reps))
-        rows["vendor_gemm_reference"] = vendor_reference(torch, dev, time_fn, args.reps, N, h, f)
+        rows.update(guarded("rows", lambda: measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph,
+                                                          args.reps)) or {})
+        vr = guarded("vendor_gemm_reference", lambda: vendor_reference(torch, dev, time_fn, args.reps, N, h, f))
+        if vr is not None:
+            rows["vendor_gemm_reference"] = vr
     torch.cuda.synchronize()
     if not args.no_rows:
-        # the matrix cores' sustained rate on this GPU with no memory traffic
-        # (random and all-zero operands), beside the step's rate
-        mr = mfma_rate()
-        med = {k: float(np.median([r["tflops"] for r in mr if r.get("data") == k])) for k in ("random", "zeros")}
-        rows["mfma_rate_no_memory"] = {"random_tflops": round(med["random"], 1), "zeros_tflops": round(med["zeros"], 1),
-                                       "step_frac_of_random": round(value / med["random"], 3)}
-        clk = device_clock(mr)
-        if clk:
-            rows["mfma_rate_no_memory"]["device_max_sclk_mhz"] = clk["max_sclk_mhz"]
-        log(f"[bench] MFMA rate without memory traffic: {rows['mfma_rate_no_memory']}")
-        # one CU's store throughput: what a GEMM tile's epilogue costs
-        sr = [r for r in run_probe("store_rate") if "pattern" in r]
-        pick = lambda pat, w, n: next(r for r in sr if r["pattern"] == pat and r["waves"] == w and r["workgroups"] == n)  # noqa: E731
-        rows["store_rate_per_cu"] = {
-            "fp32_epilogue_gbs_per_cu": {f"{n}_cus_{w}_waves": pick("epilogue_fp32", w, n)["gbs_per_workgroup"]
-                                         for n in (32, 256) for w in (4, 8, 16)},
-            "fp32_mfma_layout_gbs_per_cu": {f"{n}_cus": pick("mfma_layout_fp32", 8, n)["gbs_per_workgroup"] for n in (32, 256)},
-            "fp32_rows_gbs_per_cu_256": pick("rows_fp32", 8, 256)["gbs_per_workgroup"],
-            "bf16_epilogue_gbs_per_cu_256": pick("epilogue_bf16", 8, 256)["gbs_per_workgroup"],
-            "us_per_256x256_fp32_tile_all_cus": {
-                "swapped": round(262144 / (pick("epilogue_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2),
-                "mfma_layout": round(262144 / (pick("mfma_layout_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2)}}
-        log(f"[bench] store rate per CU: {rows['store_rate_per_cu']}")
+        guarded("probes", lambda: probe_rows(rows, value, np))
+    if errors:
+        rows["errors"] = errors
 
     # ---------------- CPU baseline: the oracle on a token sample ----------------
     cpu = None
     if args.cpu_tokens > 0:
-        cpu = cpu_baseline(d, dY_bits, args.cpu_tokens, synth, np)
+        cpu = guarded("cpu_baseline", lambda: cpu_baseline(d, dY_bits, args.cpu_tokens, synth, np))
+        if errors:
+            rows["errors"] = errors
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -744,6 +743,34 @@ def vendor_reference(torch, dev, time_fn, reps, N, h, f):
         del a, b
     log(f"[bench] vendor BLAS reference: " + ", ".join(f"{k} {v['tflops']}" for k, v in res.items()))
     return res
+
+
+def probe_rows(rows, value, np):
+    """The matrix cores' sustained rate on this GPU with no memory traffic
+    (random and all-zero operands), beside the step's rate, and one CU's
+    store throughput (what a GEMM tile's epilogue costs): both from the
+    stand-alone probes built beside the library."""
+    mr = mfma_rate()
+    med = {k: float(np.median([r["tflops"] for r in mr if r.get("data") == k])) for k in ("random", "zeros")}
+    rows["mfma_rate_no_memory"] = {"random_tflops": round(med["random"], 1), "zeros_tflops": round(med["zeros"], 1),
+                                   "step_frac_of_random": round(value / med["random"], 3)}
+    clk = device_clock(mr)
+    if clk:
+        rows["mfma_rate_no_memory"]["device_max_sclk_mhz"] = clk["max_sclk_mhz"]
+    log(f"[bench] MFMA rate without memory traffic: {rows['mfma_rate_no_memory']}")
+    # one CU's store throughput: what a GEMM tile's epilogue costs
+    sr = [r for r in run_probe("store_rate") if "pattern" in r]
+    pick = lambda pat, w, n: next(r for r in sr if r["pattern"] == pat and r["waves"] == w and r["workgroups"] == n)  # noqa: E731
+    rows["store_rate_per_cu"] = {
+        "fp32_epilogue_gbs_per_cu": {f"{n}_cus_{w}_waves": pick("epilogue_fp32", w, n)["gbs_per_workgroup"]
+                                     for n in (32, 256) for w in (4, 8, 16)},
+        "fp32_mfma_layout_gbs_per_cu": {f"{n}_cus": pick("mfma_layout_fp32", 8, n)["gbs_per_workgroup"] for n in (32, 256)},
+        "fp32_rows_gbs_per_cu_256": pick("rows_fp32", 8, 256)["gbs_per_workgroup"],
+        "bf16_epilogue_gbs_per_cu_256": pick("epilogue_bf16", 8, 256)["gbs_per_workgroup"],
+        "us_per_256x256_fp32_tile_all_cus": {
+            "swapped": round(262144 / (pick("epilogue_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2),
+            "mfma_layout": round(262144 / (pick("mfma_layout_fp32", 8, 256)["gbs_per_workgroup"] * 1e3), 2)}}
+    log(f"[bench] store rate per CU: {rows['store_rate_per_cu']}")
 
 
 def run_probe(name, *args):
