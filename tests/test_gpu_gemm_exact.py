@@ -80,7 +80,9 @@ def test_col_linear_nn_bf16_exact(N, k, n):
 # too few output tiles for the CUs (300 and 520 rows); accumulate into the
 # partial.
 SHAPES_SPLIT = [(16, 4160, 256), (40, 4160, 128), (64, 8192, 64), (3, 1024, 1280), (24, 2048, 384),
-                (16, 8192, 1280), (300, 4096, 320), (520, 6208, 640)]
+                (16, 8192, 1280), (300, 4096, 320), (520, 6208, 640),
+                # token counts that end inside a lane's 4 rows of the fp32 store
+                (301, 4096, 320), (777, 2048, 576)]
 
 
 @pytest.mark.parametrize("N,k,n", SHAPES_SPLIT)
