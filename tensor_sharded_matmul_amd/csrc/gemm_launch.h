@@ -215,6 +215,21 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
             return launch_cfg<Mid, A_T, B_KN, EPI>(fn, a, s);
         }
     }
+    if constexpr (!A_T && B_KN && EPI == EPI_F32) {
+        if (a.ksplit == 1) {
+            auto run = [&](auto mc) {
+                using MT = decltype(mc);
+                using Mid = Cfg<MT::TM, MT::TN, MT::TM, MT::TN, MT::BKA, MT::SA, MT::BKB, MT::SB, MT::WAVES_M,
+                                MT::WAVES_N>;
+                return launch_cfg<Mid, A_T, B_KN, EPI>(fn, a, s);
+            };
+            switch (mid_tile_choice<A_T, B_KN, EPI>(a.M, a.N, a.K)) {
+                case 1: return run(MidNNWide{});
+                case 2: return run(MidNNNarrow{});
+                default: break;
+            }
+        }
+    }
     // ping-pong forms: 8 waves, 128 x 64 (2 x 4) or 64 x 112 / 112 x 64
     using PSq = CfgPP<A_T, B_KN, 256, 256, 256, 256, 2, 4>;
     using PN224 = CfgPP<A_T, B_KN, 256, 256, 256, 224, 4, 2>;

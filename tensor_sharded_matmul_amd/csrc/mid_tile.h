@@ -31,17 +31,47 @@ struct MidTile<true, true> {  // 8 waves of 64 x 64, rings of 6 x 8 KB (A) and 6
     static constexpr int TM = 128, TN = 256, BKA = 32, SA = 6, BKB = 32, SB = 6, WAVES_M = 2, WAVES_N = 4;
 };
 
+// Forward fp32 products of few token rows, such as the row-parallel partial
+// in token-row chunks (the collective-matmul schedule: the GEMM2 shard of
+// Llama-3-70B in 4 or 8 chunks of 1024 or 512 tokens has 128 or 64 large
+// tiles per chunk, half or a quarter of the CUs): NN mid tiles of 128 x 256
+// or 128 x 128 give each chunk one full wave over its whole K instead of a
+// K split. They are taken only when they fill at least 7/8 of the CUs (the
+// QKV forward, 160 tiles of 128 x 256, keeps its split).
+#ifndef TPS_MID_NN
+#define TPS_MID_NN 1
+#endif
+template <int TM_, int TN_, int SB_>
+struct MidNN {  // 4 waves; A in 64-row stages of 16 KB, B in 32-row stages
+    static constexpr int TM = TM_, TN = TN_, BKA = 64, SA = 4, BKB = 32, SB = SB_, WAVES_M = 2, WAVES_N = 2;
+};
+using MidNNWide = MidNN<128, 256, 6>;    // 4 x 16 KB + 6 x 16 KB
+using MidNNNarrow = MidNN<128, 128, 8>;  // 4 x 16 KB + 8 x 8 KB
+
+// 0: no mid tile; 1: MidTile (TN) or MidNNWide (NN); 2: MidNNNarrow (NN).
+template <bool A_T, bool B_KN, int EPI>
+inline int mid_tile_choice(int M, int N, int K) {
+    const long long cus = device_cus();
+    const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    auto tiles = [&](int tm, int tn) { return (long long)((M + tm - 1) / tm) * ((N + tn - 1) / tn); };
+    if (M < 256 || K < 2048 || 2 * big > cus) return 0;
+    if constexpr (A_T && B_KN && (EPI == EPI_F32 || EPI == EPI_BF16)) {
+        using MT = MidTile<A_T, B_KN>;
+        const long long mid = tiles(MT::TM, MT::TN);
+        return 2 * mid > cus && mid <= cus ? 1 : 0;
+    } else if constexpr (!A_T && B_KN && EPI == EPI_F32 && TPS_MID_NN != 0) {
+        auto full = [&](long long t) { return 8 * t >= 7 * cus && t <= cus; };
+        if (full(tiles(MidNNWide::TM, MidNNWide::TN))) return 1;
+        if (full(tiles(MidNNNarrow::TM, MidNNNarrow::TN))) return 2;
+        return 0;
+    } else {
+        return 0;
+    }
+}
+
 template <bool A_T, bool B_KN, int EPI>
 inline bool use_mid_tile(int M, int N, int K) {
-    using MT = MidTile<A_T, B_KN>;
-    if constexpr (!MT::kOn || !(EPI == EPI_F32 || EPI == EPI_BF16)) {
-        return false;
-    } else {
-        const long long cus = device_cus();
-        const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
-        const long long mid = (long long)((M + MT::TM - 1) / MT::TM) * ((N + MT::TN - 1) / MT::TN);
-        return M >= 256 && K >= 2048 && 2 * big <= cus && 2 * mid > cus && mid <= cus;
-    }
+    return mid_tile_choice<A_T, B_KN, EPI>(M, N, K) != 0;
 }
 
 }  // namespace tps

@@ -1,8 +1,9 @@
 """The row-parallel partial in row chunks (tp_row_linear_partial_chunked):
 exact against the oracle on integer inputs for several chunk counts (chunks
 that need split-K included), with and without accumulate, every chunk's event
-recorded in chunk order; at the Llama-3-70B GEMM2 shape, every element of
-every chunk count against the fp64 oracle within the tolerance."""
+recorded in chunk order; chunk-sized products on the NN mid tiles exact; at
+the Llama-3-70B GEMM2 shape, every element of every chunk count against the
+fp64 oracle within the tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -30,6 +31,26 @@ def test_chunked_partial_exact(N, k, n, nchunks, accumulate):
     assert all(e.query() for e in events)
     for a, b in zip(events, events[1:]):
         assert a.elapsed_time(b) >= 0.0
+
+
+# Chunk-sized fp32 row partials take NN mid tiles (128 x 256 when they fill
+# a wave of the 256 CUs, else 128 x 128) over their whole K: the GEMM2 shard
+# in 4 chunks (1024 tokens) and 8 chunks (512), here ragged on every edge
+# (the last row tile partly filled, widths ending inside a tile) and exact.
+@pytest.mark.parametrize("N,k,n", [(1000, 2112, 7936), (500, 2048, 7680), (1024, 2048, 8192), (512, 2048, 8192)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_chunk_sized_partial_mid_tiles_exact(N, k, n, accumulate):
+    assert T.workspace_size("tp_row_linear_partial", N, k, n) == 0   # no K split
+    Zb, Wb = synth.int_inputs(90, (N, k)), synth.int_inputs(91, (k, n))
+    P0 = synth.bf16_to_f64(synth.int_inputs(92, (N, n)))
+    big = torch.full((N * n + 256,), 12345.0, dtype=torch.float32, device="cuda:0")
+    P = big[:N * n].view(N, n)
+    P.copy_(torch.from_numpy(P0.astype(np.float32)))
+    T.tp_row_linear_partial(to_dev(Zb), to_dev(Wb), P=P, accumulate=accumulate)
+    torch.cuda.synchronize()
+    want = O.row_linear_partial(synth.bf16_to_f64(Zb), synth.bf16_to_f64(Wb)) + (P0 if accumulate else 0)
+    assert np.array_equal(f64(P), want)
+    assert bool(torch.all(big[N * n:] == 12345.0))
 
 
 def test_chunked_llama_gemm2_against_oracle():
