@@ -205,6 +205,14 @@ def test_workspace_query_values():
     assert T.workspace_size("tp_row_linear_bwd", 3000, 2112, 1984) == 0
     # dO of the attention shard at 4096 tokens splits (64 large tiles)
     assert T.workspace_size("tp_row_linear_bwd", 4096, 1024, 8192) > 0
+    # the GEMM2 shard in 4 and 8 token-row chunks (1024 and 512 rows): NN mid
+    # tiles of 128 x 256 and 128 x 128 fill the 256 CUs, no split; 16 chunks
+    # (256 rows) fill neither and split
+    assert T.workspace_size("tp_row_linear_partial", 1024, 3584, 8192) == 0
+    assert T.workspace_size("tp_row_linear_partial", 512, 3584, 8192) == 0
+    assert T.workspace_size("tp_row_linear_partial", 256, 3584, 8192) > 0
+    # the QKV forward keeps its split (160 mid tiles would leave 96 CUs idle)
+    assert T.workspace_size("tp_col_linear", 4096, 8192, 1280, 0) == 3 * 4096 * 1280 * 4
     # products with enough output tiles need none
     assert T.workspace_size("tp_mlp_shard_fwd", 4096, 8192, 3584, 2) == 0
     assert T.workspace_size("tp_mlp_shard_bwd", 4096, 8192, 3584, 2) == 0
