@@ -385,6 +385,27 @@ def main() -> int:
                             "overhead": round(ms_c / kt["gemm2_down_partial"]["ms"] - 1, 3)}
     if chunked:
         kt["gemm2_down_partial_chunked"] = chunked
+    # dX_part of the backward in token-row chunks (its exchange could start
+    # chunk by chunk), then the same followed by dW_gate|up over all tokens
+    # against the unchunked column-parallel backward of both
+    chunked = {}
+    for nc in (() if args.no_rows else (2, 4, 8)):
+        evs = [torch.cuda.Event() for _ in range(nc)]
+
+        def dxc():
+            T.tp_col_linear_bwd_chunked(X, W_in, dH, nc, dX_part=dX, want_dw=False, events=evs)
+
+        ms_c = time_fn(dxc, args.reps)[0]
+        chunked[str(nc)] = {"ms": round(ms_c, 4), "tflops": round(fl["bwd_dx_partial"] / (ms_c * 1e-3) / 1e12, 1),
+                            "overhead": round(ms_c / kt["bwd_dx_partial"]["ms"] - 1, 3)}
+    if chunked:
+        kt["bwd_dx_partial_chunked"] = chunked
+        evs = [torch.cuda.Event() for _ in range(8)]
+        ms_both = time_fn(lambda: T.tp_col_linear_bwd(X, W_in, dH, dX_part=dX, dW=dWi), args.reps)[0]
+        ms_c8 = time_fn(lambda: T.tp_col_linear_bwd_chunked(X, W_in, dH, 8, dX_part=dX, dW=dWi, events=evs),
+                        args.reps)[0]
+        kt["col_bwd_dx_8_chunks_then_dw"] = {"ms": round(ms_c8, 4), "unchunked_ms": round(ms_both, 4),
+                                             "overhead": round(ms_c8 / ms_both - 1, 3)}
 
     # The fp32 epilogue's cost: GEMM2's output shape (512 tiles of 256 x 256,
     # two waves on 256 CUs) contracted over K = 64, two k32 sub-steps, so a

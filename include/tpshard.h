@@ -233,6 +233,29 @@ tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The column-parallel backward with dX_part computed in row chunks, for
+ * hiding its exchange ([TPSP] "把通信藏到计算后面": a column-parallel layer's
+ * dX exchange can run while dW = X^T dY, which does not need it, is computed;
+ * an output cut into chunks can be sent a chunk at a time). The results are
+ * those of tp_col_linear_bwd. dX_part comes first, in nchunks chunks of
+ * token rows (ceil(N / nchunks) rows rounded up to 16; the last may be
+ * shorter or empty); after chunk c is enqueued, events[c] (a caller-created
+ * hipEvent_t) is recorded on `stream`, so another stream can wait for
+ * exactly that chunk. Then dW, over all N tokens, when dW is not NULL.
+ * events may be NULL (no events). dX_part must not be NULL; accumulate != 0
+ * adds into dX_part only. 1 <= nchunks <= 64. The chunks and dW use the
+ * workspace one after another; the query counts dW.
+ */
+tp_status tp_col_linear_bwd_chunked_workspace_size(int64_t N, int64_t k, int64_t n,
+                                                   int32_t nchunks, size_t* bytes);
+tp_status tp_col_linear_bwd_chunked(const void* X, const void* W, const void* dY,
+                                    float* dX_part, float* dW,
+                                    int64_t N, int64_t k, int64_t n, int accumulate,
+                                    int32_t nchunks, void* const* events,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * Row-parallel linear, backward ([TPSP] "矩阵乘法的两种切法": both gradients are
  * local). Used for the attention output projection W_O.
  *   Z bf16 [N,k_loc], W bf16 [k_loc,n], dY bf16 [N,n]

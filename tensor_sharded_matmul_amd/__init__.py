@@ -21,7 +21,7 @@ __all__ = [
     "lib_path", "load", "tp_version", "tp_last_error", "tp_col_linear",
     "tp_row_linear_partial", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
     "tp_col_linear_bwd", "tp_row_linear_bwd", "tp_qkv_regroup", "tp_shard_shape",
-    "tp_row_linear_partial_chunked", "tp_kv_grad_accumulate", "tp_vocab_ce_fwd",
+    "tp_row_linear_partial_chunked", "tp_col_linear_bwd_chunked", "tp_kv_grad_accumulate", "tp_vocab_ce_fwd",
     "tp_vocab_ce_combine", "tp_vocab_ce_bwd", "tp_vocab_embed_fwd", "tp_vocab_embed_bwd",
     "tp_col_linear_noalloc", "workspace_size", "regroup_width", "ACT", "TPError",
 ]
@@ -70,6 +70,9 @@ def load():
         "tp_mlp_shard_bwd": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i, vp, vp, vp, vp, i, vp, sz, vp], i),
         "tp_col_linear_bwd_workspace_size": ([i64, i64, i64, psz], i),
         "tp_col_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, i, vp, sz, vp], i),
+        "tp_col_linear_bwd_chunked_workspace_size": ([i64, i64, i64, i32, psz], i),
+        "tp_col_linear_bwd_chunked": ([vp, vp, vp, vp, vp, i64, i64, i64, i, i32, ctypes.POINTER(vp), vp, sz,
+                                       vp], i),
         "tp_row_linear_bwd_workspace_size": ([i64, i64, i64, psz], i),
         "tp_row_linear_bwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], i),
         "tp_qkv_regroup": ([vp, vp, i64, i32, i32, i32, i32, i32, vp], i),
@@ -225,6 +228,18 @@ def tp_row_linear_partial(Z, W, P=None, accumulate=False, workspace=None, stream
     return P
 
 
+def _events(events, nchunks):
+    """None, or a C array of the HIP events of `events` (nchunks torch.cuda.Event)."""
+    if events is None:
+        return None
+    if len(events) != nchunks:
+        raise ValueError(f"{len(events)} events for {nchunks} chunks")
+    for e in events:
+        if not e.cuda_event:  # torch creates the HIP event on its first record
+            e.record()
+    return (ctypes.c_void_p * nchunks)(*[e.cuda_event for e in events])
+
+
 def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, events=None, workspace=None,
                                   stream=None):
     """P = Z W (or P += Z W) in nchunks token-row chunks; events: None or nchunks
@@ -235,14 +250,7 @@ def tp_row_linear_partial_chunked(Z, W, nchunks, P=None, accumulate=False, event
     _dev(Z, "Z", _bf16, (N, k_loc))
     _dev(W, "W", _bf16, (k_loc, n))
     P = _out(P, "P", _f32, (N, n), Z)
-    ev = None
-    if events is not None:
-        if len(events) != nchunks:
-            raise ValueError(f"{len(events)} events for {nchunks} chunks")
-        for e in events:
-            if not e.cuda_event:  # torch creates the HIP event on its first record
-                e.record()
-        ev = (ctypes.c_void_p * nchunks)(*[e.cuda_event for e in events])
+    ev = _events(events, nchunks)
     wp, wn, _keep = _workspace("tp_row_linear_partial_chunked", (N, k_loc, n, nchunks), Z, stream, workspace)
     _check(lib.tp_row_linear_partial_chunked(_ptr(Z), _ptr(W), _ptr(P), N, k_loc, n, int(bool(accumulate)),
                                              nchunks, ev, wp, wn, _stream(stream)))
@@ -320,6 +328,27 @@ def tp_col_linear_bwd(X, W, dY, dX_part=None, dW=None, want_dx=True, want_dw=Tru
                                  _ptr(dW if want_dw else None), N, k, n, int(bool(accumulate)), wp, wn,
                                  _stream(stream)))
     return (dX_part if want_dx else None), (dW if want_dw else None)
+
+
+def tp_col_linear_bwd_chunked(X, W, dY, nchunks, dX_part=None, dW=None, want_dw=True, accumulate=False,
+                              events=None, workspace=None, stream=None):
+    """dX_part = dY W^T ({U}; accumulate adds) in nchunks token-row chunks,
+    events[c] recorded after chunk c, then dW = X^T dY over all tokens;
+    returns (dX_part, dW)."""
+    lib = load()
+    N, k = X.shape
+    n = W.shape[1]
+    _dev(X, "X", _bf16, (N, k))
+    _dev(W, "W", _bf16, (k, n))
+    _dev(dY, "dY", _bf16, (N, n))
+    dX_part = _out(dX_part, "dX_part", _f32, (N, k), X)
+    if want_dw:
+        dW = _out(dW, "dW", _f32, (k, n), X)
+    ev = _events(events, nchunks)
+    wp, wn, _keep = _workspace("tp_col_linear_bwd_chunked", (N, k, n, nchunks), X, stream, workspace)
+    _check(lib.tp_col_linear_bwd_chunked(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX_part), _ptr(dW if want_dw else None),
+                                         N, k, n, int(bool(accumulate)), nchunks, ev, wp, wn, _stream(stream)))
+    return dX_part, (dW if want_dw else None)
 
 
 def tp_row_linear_bwd(Z, W, dY, dZ=None, dW=None, want_dz=True, want_dw=True, workspace=None, stream=None):

@@ -215,7 +215,7 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
             return launch_cfg<Mid, A_T, B_KN, EPI>(fn, a, s);
         }
     }
-    if constexpr (!A_T && B_KN && EPI == EPI_F32) {
+    if constexpr (!A_T && EPI == EPI_F32) {
         if (a.ksplit == 1) {
             auto run = [&](auto mc) {
                 using MT = decltype(mc);
@@ -223,9 +223,12 @@ tp_status launch_by_shape(const char* fn, const GemmArgs& a, hipStream_t s) {
                                 MT::WAVES_N>;
                 return launch_cfg<Mid, A_T, B_KN, EPI>(fn, a, s);
             };
+            using Wide = typename std::conditional<B_KN, MidNNWide, MidNTWide>::type;
             switch (mid_tile_choice<A_T, B_KN, EPI>(a.M, a.N, a.K)) {
-                case 1: return run(MidNNWide{});
-                case 2: return run(MidNNNarrow{});
+                case 1: return run(Wide{});
+                case 2:
+                    if constexpr (B_KN) return run(MidNNNarrow{});
+                    break;
                 default: break;
             }
         }

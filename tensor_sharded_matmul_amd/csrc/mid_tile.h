@@ -48,7 +48,22 @@ struct MidNN {  // 4 waves; A in 64-row stages of 16 KB, B in 32-row stages
 using MidNNWide = MidNN<128, 256, 6>;    // 4 x 16 KB + 6 x 16 KB
 using MidNNNarrow = MidNN<128, 128, 8>;  // 4 x 16 KB + 8 x 8 KB
 
-// 0: no mid tile; 1: MidTile (TN) or MidNNWide (NN); 2: MidNNNarrow (NN).
+// The same for the NT fp32 products of few token rows, on the wide tile
+// only: dX_part of the column-parallel backward in token-row chunks. The MLP
+// shard's dX of Llama-3-70B in 4 chunks of 1024 tokens: 423-425 us against
+// 472-475 us for the K split alone, 794-798 against 813-815 us followed by
+// dW (three interleaved runs). 128 x 128 tiles for 8 chunks of 512 tokens
+// were faster alone (534 against 548 us) but slower followed by dW (928
+// against 918 us): those keep the split.
+#ifndef TPS_MID_NT
+#define TPS_MID_NT 1
+#endif
+struct MidNTWide {  // 4 waves; both operands in 64-row stages, 4 x 16 KB + 3 x 32 KB
+    static constexpr int TM = 128, TN = 256, BKA = 64, SA = 4, BKB = 64, SB = 3, WAVES_M = 2, WAVES_N = 2;
+};
+
+// 0: no mid tile; 1: MidTile (TN), MidNNWide (NN) or MidNTWide (NT);
+// 2: MidNNNarrow (NN).
 template <bool A_T, bool B_KN, int EPI>
 inline int mid_tile_choice(int M, int N, int K) {
     const long long cus = device_cus();
@@ -59,15 +74,19 @@ inline int mid_tile_choice(int M, int N, int K) {
         using MT = MidTile<A_T, B_KN>;
         const long long mid = tiles(MT::TM, MT::TN);
         return 2 * mid > cus && mid <= cus ? 1 : 0;
-    } else if constexpr (!A_T && B_KN && EPI == EPI_F32 && TPS_MID_NN != 0) {
+    } else if constexpr (!A_T && EPI == EPI_F32 && (B_KN ? TPS_MID_NN != 0 : TPS_MID_NT != 0)) {
+        // (the wide tiles have the same shape on both layouts)
         auto full = [&](long long t) { return 8 * t >= 7 * cus && t <= cus; };
         if (full(tiles(MidNNWide::TM, MidNNWide::TN))) return 1;
-        if (full(tiles(MidNNNarrow::TM, MidNNNarrow::TN))) return 2;
+        if (B_KN && full(tiles(MidNNNarrow::TM, MidNNNarrow::TN))) return 2;
         return 0;
     } else {
         return 0;
     }
 }
+
+static_assert(MidNTWide::TM == MidNNWide::TM && MidNTWide::TN == MidNNWide::TN,
+              "mid_tile_choice counts the NN wide tile shape for both layouts");
 
 template <bool A_T, bool B_KN, int EPI>
 inline bool use_mid_tile(int M, int N, int K) {

@@ -738,10 +738,23 @@ static tp_status row_partial_plan(const char* fn, const void* Z, const void* W, 
 
 // chunk c of the chunked row partial: token rows [c rows, (c + 1) rows),
 // rows = ceil(N / nchunks) rounded up to 16
+// Token rows [r0, r1) of chunk c when N rows are cut into nchunks chunks of
+// ceil(N / nchunks) rows rounded up to 16 (the last may be shorter or empty).
+static void chunk_rows(int64_t N, int nchunks, int c, int64_t& r0, int64_t& r1) {
+    const int64_t rows = ((N + nchunks - 1) / nchunks + 15) / 16 * 16;
+    r0 = std::min<int64_t>(N, c * rows);
+    r1 = std::min<int64_t>(N, r0 + rows);
+}
+
+static tp_status check_nchunks(const char* fn, int32_t nchunks) {
+    if (nchunks < 1 || nchunks > 64) return fail(TP_ERR_INVALID_ARG, "%s: nchunks = %d outside [1, 64]", fn, nchunks);
+    return TP_OK;
+}
+
 static GemmArgs row_chunk(const void* Z, const void* W, float* P, int64_t N, int64_t k_loc, int64_t n,
                           int accumulate, int nchunks, int c) {
-    const int64_t rows = ((N + nchunks - 1) / nchunks + 15) / 16 * 16;
-    const int64_t r0 = std::min<int64_t>(N, c * rows), r1 = std::min<int64_t>(N, r0 + rows);
+    int64_t r0, r1;
+    chunk_rows(N, nchunks, c, r0, r1);
     GemmArgs a = make_args(Z ? static_cast<const uint16_t*>(Z) + r0 * k_loc : nullptr, W, P ? P + r0 * n : nullptr,
                            (int)(r1 - r0), (int)n, (int)k_loc, (int)k_loc, (int)n, (int)n);
     a.accumulate = accumulate ? 1 : 0;
@@ -753,7 +766,7 @@ static tp_status row_chunked_plan(const char* fn, int64_t N, int64_t k_loc, int6
     TP_TRY(check_tokens(fn, N));
     TP_TRY(check_width(fn, "k_loc", k_loc));
     TP_TRY(check_width(fn, "n", n));
-    if (nchunks < 1 || nchunks > 64) return fail(TP_ERR_INVALID_ARG, "%s: nchunks = %d outside [1, 64]", fn, nchunks);
+    TP_TRY(check_nchunks(fn, nchunks));
     TP_TRY(check_elems(fn, N, k_loc));
     TP_TRY(check_elems(fn, k_loc, n));
     TP_TRY(check_elems(fn, N, n));
@@ -833,6 +846,33 @@ static tp_status col_bwd_plan(const char* fn, const void* X, const void* W, cons
     b = make_args(X, dY, dW, (int)k, (int)n, (int)N, (int)k, (int)n, (int)n);
     need = need_of({(query || dX_part) ? plan_of<false, false, EPI_F32>(a) : SplitPlan{},
                     (query || dW) ? plan_of<true, true, EPI_F32>(b) : SplitPlan{}});
+    return TP_OK;
+}
+
+// Chunk c of the chunked column-parallel backward: dY's token rows [r0, r1)
+// times W^T into the same rows of dX_part.
+static GemmArgs col_dx_chunk(const void* dY, const void* W, float* dX_part, int64_t N, int64_t k, int64_t n,
+                             int accumulate, int nchunks, int c) {
+    int64_t r0, r1;
+    chunk_rows(N, nchunks, c, r0, r1);
+    GemmArgs a = make_args(dY ? static_cast<const uint16_t*>(dY) + r0 * n : nullptr, W,
+                           dX_part ? dX_part + r0 * k : nullptr, (int)(r1 - r0), (int)k, (int)n, (int)n, (int)n,
+                           (int)k);
+    a.accumulate = accumulate ? 1 : 0;
+    return a;
+}
+
+// dW (b, over all N tokens) and the validation of the chunked call; the
+// chunks and dW run one after another and reuse one workspace.
+static tp_status col_bwd_chunked_plan(const char* fn, const void* X, const void* dY, float* dW, int64_t N, int64_t k,
+                                      int64_t n, int32_t nchunks, bool query, GemmArgs& b, size_t& need) {
+    GemmArgs a;
+    TP_TRY(col_bwd_plan(fn, X, nullptr, dY, nullptr, dW, N, k, n, 0, query, a, b, need));
+    TP_TRY(check_nchunks(fn, nchunks));
+    need = (query || dW) ? plan_of<true, true, EPI_F32>(b).bytes : 0;
+    for (int c = 0; c < nchunks; ++c)
+        need = std::max(need, plan_of<false, false, EPI_F32>(col_dx_chunk(nullptr, nullptr, nullptr, N, k, n, 0,
+                                                                          nchunks, c)).bytes);
     return TP_OK;
 }
 
@@ -1129,6 +1169,46 @@ tp_status tp_col_linear_bwd(const void* X, const void* W, const void* dY, float*
     TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dX_part) TP_TRY((run_gemm<false, false, EPI_F32>(fn, a, workspace, s)));
+    if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, workspace, s)));
+    return ok();
+}
+
+tp_status tp_col_linear_bwd_chunked_workspace_size(int64_t N, int64_t k, int64_t n, int32_t nchunks,
+                                                   size_t* bytes) {
+    const char* fn = "tp_col_linear_bwd_chunked_workspace_size";
+    TP_QUERY_OUT(bytes);
+    GemmArgs b;
+    size_t need = 0;
+    TP_TRY(col_bwd_chunked_plan(fn, nullptr, nullptr, nullptr, N, k, n, nchunks, true, b, need));
+    *bytes = need;
+    return ok();
+}
+
+tp_status tp_col_linear_bwd_chunked(const void* X, const void* W, const void* dY, float* dX_part, float* dW,
+                                    int64_t N, int64_t k, int64_t n, int accumulate, int32_t nchunks,
+                                    void* const* events, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "tp_col_linear_bwd_chunked";
+    GemmArgs b;
+    size_t need = 0;
+    TP_TRY(col_bwd_chunked_plan(fn, X, dY, dW, N, k, n, nchunks, false, b, need));
+    TP_CHECK_TOK_PTR(dY, "dY");
+    TP_CHECK_TOK_PTR(dX_part, "dX_part");
+    TP_CHECK_PTR(W, "W");
+    TP_CHECK_OPT_PTR(dW, "dW");
+    if (dW) TP_CHECK_TOK_PTR(X, "X");
+    if (events)
+        for (int c = 0; c < nchunks; ++c)
+            if (!events[c]) return fail(TP_ERR_INVALID_ARG, "%s: events[%d] is NULL", fn, c);
+    TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int c = 0; c < nchunks; ++c) {
+        TP_TRY((run_gemm<false, false, EPI_F32>(fn, col_dx_chunk(dY, W, dX_part, N, k, n, accumulate, nchunks, c),
+                                                workspace, s)));
+        if (events) {
+            hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[c]), s);
+            if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: event %d: %s", fn, c, hipGetErrorString(e));
+        }
+    }
     if (dW) TP_TRY((run_gemm<true, true, EPI_F32>(fn, b, workspace, s)));
     return ok();
 }

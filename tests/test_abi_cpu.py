@@ -116,6 +116,12 @@ def test_vocab_calls_validate_before_launch():
     assert comb(NULL, NULL, NULL, 0, 16, NULL, NULL, NULL, NULL) == 1               # t = 0
     ch = _raw("tp_row_linear_partial_chunked")
     assert ch(NULL, NULL, NULL, 16, 1024, 8192, 0, 0, NULL, NULL, 0, NULL) == 1     # nchunks = 0
+    cb = _raw("tp_col_linear_bwd_chunked")
+    assert cb(NULL, NULL, NULL, NULL, NULL, 16, 1024, 8192, 0, 65, NULL, NULL, 0, NULL) == 1  # nchunks = 65
+    p = ctypes.c_void_p(0x10000)
+    assert cb(p, p, p, NULL, p, 16, 1024, 8192, 0, 2, NULL, NULL, 0, NULL) == 1      # NULL dX_part
+    assert "dX_part" in T.tp_last_error()
+    assert cb(NULL, p, p, p, p, 16, 1024, 8192, 0, 2, NULL, NULL, 0, NULL) == 1      # dW without X
 
 
 def test_regroup_width_matches_oracle():
@@ -153,6 +159,7 @@ WS_CASES = {
     "tp_col_linear": (16, 8192, 1280, 0),
     "tp_row_linear_partial": (16, 8192, 8192),
     "tp_row_linear_partial_chunked": (48, 8192, 8192, 3),
+    "tp_col_linear_bwd_chunked": (4096, 8192, 7168, 8),   # dX of the MLP shard in 512-row chunks
     "tp_mlp_shard_fwd": (16, 8192, 3584, 2),
     "tp_row_linear_bwd": (4096, 512, 8192),      # W_O of Llama-3-70B at t = 16
     "tp_vocab_ce_fwd": (4096, 8192, 16128),
@@ -211,6 +218,15 @@ def test_workspace_query_values():
     assert T.workspace_size("tp_row_linear_partial", 1024, 3584, 8192) == 0
     assert T.workspace_size("tp_row_linear_partial", 512, 3584, 8192) == 0
     assert T.workspace_size("tp_row_linear_partial", 256, 3584, 8192) > 0
+    # dX of the MLP shard (dH [4096, 7168] W_gate|up^T) in row chunks: 2
+    # chunks of 2048 rows fill the CUs with 256 x 256 tiles, 4 chunks (1024
+    # rows) with NT mid tiles of 128 x 256, no split; 8 chunks (512 rows)
+    # split, needing what one 512-row product needs (dW over 4096 tokens
+    # needs none)
+    for nc in (2, 4):
+        assert T.workspace_size("tp_col_linear_bwd_chunked", 4096, 8192, 7168, nc) == 0
+    n8 = T.workspace_size("tp_col_linear_bwd_chunked", 4096, 8192, 7168, 8)
+    assert n8 == T.workspace_size("tp_col_linear_bwd", 512, 8192, 7168) > 0
     # the QKV forward keeps its split (160 mid tiles would leave 96 CUs idle)
     assert T.workspace_size("tp_col_linear", 4096, 8192, 1280, 0) == 3 * 4096 * 1280 * 4
     # products with enough output tiles need none
