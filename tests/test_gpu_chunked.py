@@ -7,7 +7,9 @@ fp64 oracle within the tolerance. The column-parallel backward with dX_part
 in row chunks (tp_col_linear_bwd_chunked) the same way: exact dX_part and dW
 on integer inputs (chunks that split K, empty chunks, accumulate), events in
 order and before dW's completion, and the Llama-3-70B MLP shard's dX at every
-element for 2, 4 and 8 chunks."""
+element for 2, 4 and 8 chunks. For both calls, a second stream that waits for
+each chunk's event and copies that chunk out (what an exchange would do)
+sees every chunk finished."""
 import numpy as np
 import pytest
 import torch
@@ -142,3 +144,32 @@ def test_chunked_llama_mlp_dx_against_oracle():
         errs[f"dX_part, {nchunks} chunks"] = err(f64(dX), want)
         del dX
     check_errs(errs, "llama70b MLP dX chunked (every element)")
+
+
+@pytest.mark.parametrize("which", ["row_partial", "col_bwd"])
+def test_chunk_events_gate_a_consumer_stream(which):
+    # The use the events are for: a second stream (the exchange) waits for
+    # chunk c's event, then reads chunk c's rows while later chunks are
+    # still computed. Here the reading is a copy; every copied chunk must be
+    # the finished one.
+    N, k, n, nchunks = 2048, 1024, 2048, 4
+    A, Bm = synth.int_inputs(96, (N, k)), synth.int_inputs(97, (k, n))
+    events = [torch.cuda.Event() for _ in range(nchunks)]
+    # (filled before the call, so every event follows the fill)
+    copy = torch.full((N, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    if which == "row_partial":
+        out = T.tp_row_linear_partial_chunked(to_dev(A), to_dev(Bm), nchunks, events=events)
+        want = O.row_linear_partial(synth.bf16_to_f64(A), synth.bf16_to_f64(Bm))
+    else:
+        X = torch.empty((N, n), dtype=torch.bfloat16, device="cuda:0")   # dX only: X not read
+        out, _ = T.tp_col_linear_bwd_chunked(X, to_dev(Bm.T.copy()), to_dev(A), nchunks, want_dw=False,
+                                             events=events)
+        want, _ = O.col_linear_bwd(np.zeros((N, n)), synth.bf16_to_f64(Bm.T.copy()), synth.bf16_to_f64(A))
+    rows = ((N + nchunks - 1) // nchunks + 15) // 16 * 16   # the calls' chunk height
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for c in range(nchunks):
+            side.wait_event(events[c])
+            copy[c * rows:(c + 1) * rows].copy_(out[c * rows:(c + 1) * rows])
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(copy), want)
