@@ -173,3 +173,17 @@ def test_chunk_events_gate_a_consumer_stream(which):
             copy[c * rows:(c + 1) * rows].copy_(out[c * rows:(c + 1) * rows])
     torch.cuda.synchronize()
     assert np.array_equal(f64(copy), want)
+
+
+def test_chunked_col_bwd_no_tokens():
+    # N = 0: every chunk is empty; dW contracts over no tokens and is zero
+    k, n = 512, 640
+    X = torch.empty((0, k), dtype=torch.bfloat16, device="cuda:0")
+    dY = torch.empty((0, n), dtype=torch.bfloat16, device="cuda:0")
+    dW = torch.full((k, n), 7.0, dtype=torch.float32, device="cuda:0")
+    events = [torch.cuda.Event() for _ in range(3)]
+    dX, dW = T.tp_col_linear_bwd_chunked(X, to_dev(synth.int_inputs(98, (k, n))), dY, 3, dW=dW, events=events)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, k)
+    assert bool(torch.all(dW == 0.0))
+    assert all(e.query() for e in events)
