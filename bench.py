@@ -110,6 +110,10 @@ def parse():
     ap.add_argument("--mfma-rate", action="store_true",
                     help="only run the MFMA rate probe (bf16 16x16x32 MFMAs on register operands, no memory "
                          "traffic; random and all-zero data) and print its JSON lines, then exit")
+    ap.add_argument("--chunked-only", type=int, default=0, metavar="CALLS",
+                    help="only run the chunked schedule on the Llama-3-70B MLP shard CALLS times: GEMM2 in 1, 2, "
+                         "4 and 8 token-row chunks, dX_part in 1, 2, 4 and 8 chunks, then dX_part in 8 chunks "
+                         "followed by dW_gate|up (for profiling), then exit")
     ap.add_argument("--decode-only", type=int, default=0, metavar="CALLS",
                     help="only run the decode-sized (16 tokens) QKV and W_O products of the Llama-3-70B "
                          "attention shard CALLS times (16 rotated weight copies; for profiling), then exit")
@@ -186,6 +190,25 @@ def main() -> int:
                 torch.matmul(a_, b_)
         torch.cuda.synchronize()
         log(f"[bench] attention prefill products run {args.attn_prefill_only} times")
+        return 0
+    if args.chunked_only:
+        w = synth.WORKLOADS["llama70b_swiglu_t8"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed)
+        rnd = lambda *shape: torch.randn(shape, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+        Xc, Wg, Zc, Wd, dHc = rnd(w.N, w.h), rnd(w.h, 2 * w.f), rnd(w.N, w.f), rnd(w.f, w.h), rnd(w.N, 2 * w.f)
+        Pc = torch.empty((w.N, w.h), device=dev, dtype=torch.float32)
+        dXc = torch.empty((w.N, w.h), device=dev, dtype=torch.float32)
+        dWc = torch.empty((w.h, 2 * w.f), device=dev, dtype=torch.float32)
+        evs = {nc: [torch.cuda.Event() for _ in range(nc)] for nc in (1, 2, 4, 8)}
+        for _ in range(args.chunked_only):
+            for nc in (1, 2, 4, 8):
+                T.tp_row_linear_partial_chunked(Zc, Wd, nc, P=Pc, events=evs[nc])
+            for nc in (1, 2, 4, 8):
+                T.tp_col_linear_bwd_chunked(Xc, Wg, dHc, nc, dX_part=dXc, want_dw=False, events=evs[nc])
+            T.tp_col_linear_bwd_chunked(Xc, Wg, dHc, 8, dX_part=dXc, dW=dWc, events=evs[8])
+        torch.cuda.synchronize()
+        log(f"[bench] chunked schedule run {args.chunked_only} times")
         return 0
     if args.decode_only:
         q = synth.WORKLOADS["llama70b_qkv_t8"]
