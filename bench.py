@@ -84,10 +84,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # 1000 steps: the timed region lasts about 1.7 s, long enough for an
-    # outside sampler of GPU activity to see it (20 and 2000 steps gave the
-    # same time per step, within 0.1 %)
-    ap.add_argument("--steps", type=int, default=1000)
+    # 3000 steps: the timed region lasts about 5 s, long enough for an
+    # outside sampler of GPU activity to see it (20, 2000 and 20000 steps
+    # gave the same time per step, within 0.2 %)
+    ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=10, help="repetitions per single-kernel timing")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
