@@ -1,7 +1,8 @@
 """Calls captured into a HIP graph and replayed give the same bits as the same
 calls run eagerly: the split-K decode products (their workspace allocated by
-the binding inside the capture), the MLP forward at decode size and the
-fused-QKV regroup. Capture works on a fresh stream, with no call before it.
+the binding inside the capture), the MLP forward at decode size, the
+fused-QKV regroup, and both chunked calls with their per-chunk events.
+Capture works on a fresh stream, with no call before it.
 Each replay follows eager work that rewrites the inputs in place, and every
 replay is checked."""
 import numpy as np
@@ -103,4 +104,56 @@ def test_replay_after_larger_eager_calls_on_the_capture_stream():
         torch.cuda.synchronize()
         assert err(f64(Y), want) <= TOL, r
         assert err(f64(Yb), O.col_linear(f64(Xb), f64(Wb))) <= TOL, r
+    del graph
+
+
+@pytest.mark.parametrize("nchunks", [2, 8])
+def test_chunked_calls_with_events_captured(nchunks):
+    # Both chunked calls, their events recorded on the capturing stream (and
+    # the split products' workspace allocated inside the capture), replayed
+    # after eager work that rewrites an input in place: every replay equals
+    # the eager calls, which equal the oracle (integer inputs: exact).
+    dev = "cuda:0"
+    N, k, n = 2048, 1024, 2048
+    A = to_dev(synth.int_inputs(70, (N, k)))
+    B = to_dev(synth.int_inputs(71, (k, n)))
+    Xc = to_dev(synth.int_inputs(72, (N, n)))
+    Wc = to_dev(synth.int_inputs(73, (n, k)))
+    P = torch.empty((N, n), device=dev, dtype=torch.float32)
+    dX = torch.empty((N, n), device=dev, dtype=torch.float32)
+    dW = torch.empty((n, k), device=dev, dtype=torch.float32)
+    evs = [torch.cuda.Event() for _ in range(2 * nchunks)]
+    for e in evs:            # created before the capture
+        e.record()
+    torch.cuda.synchronize()
+
+    def calls():
+        T.tp_row_linear_partial_chunked(A, B, nchunks, P=P, events=evs[:nchunks])
+        T.tp_col_linear_bwd_chunked(Xc, Wc, A, nchunks, dX_part=dX, dW=dW, events=evs[nchunks:])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    outs = (P, dX, dW)
+    for r in range(3):
+        a_host = synth.int_inputs(74 + r, (N, k))
+        A.copy_(to_dev(a_host))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(0)
+        calls()
+        torch.cuda.synchronize()
+        for g, e in zip(got, outs):
+            assert torch.equal(g.view(torch.int32), e.view(torch.int32)), r
+        a64 = synth.bf16_to_f64(a_host)
+        assert np.array_equal(f64(P), O.row_linear_partial(a64, synth.bf16_to_f64(synth.int_inputs(71, (k, n)))))
+        want_dx, want_dw = O.col_linear_bwd(synth.bf16_to_f64(synth.int_inputs(72, (N, n))),
+                                            synth.bf16_to_f64(synth.int_inputs(73, (n, k))), a64)
+        assert np.array_equal(f64(dX), want_dx) and np.array_equal(f64(dW), want_dw), r
     del graph
