@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("N,k,n,nchunks", [(1000, 512, 640, 1), (1000, 512, 640, 3), (1000, 2048, 640, 8),
-                                           (37, 256, 128, 4), (300, 4096, 320, 2)])
+                                           (37, 256, 128, 4), (300, 4096, 320, 2), (1000, 512, 640, 64)])
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_chunked_partial_exact(N, k, n, nchunks, accumulate):
     Zb, Wb = synth.int_inputs(80, (N, k)), synth.int_inputs(81, (k, n))
@@ -95,7 +95,8 @@ def test_chunk_sized_dx_mid_tiles_exact(N, k, n, accumulate):
     assert bool(torch.all(big[N * k:] == 12345.0))
 
 @pytest.mark.parametrize("N,k,n,nchunks", [(1000, 512, 640, 3), (1000, 2048, 640, 8), (37, 256, 128, 4),
-                                           (300, 4096, 320, 2), (1024, 2048, 4096, 4), (1000, 640, 2048, 1)])
+                                           (300, 4096, 320, 2), (1024, 2048, 4096, 4), (1000, 640, 2048, 1),
+                                           (1000, 512, 640, 64)])
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_chunked_col_bwd_exact(N, k, n, nchunks, accumulate):
     Xb, Wb, dYb = synth.int_inputs(83, (N, k)), synth.int_inputs(84, (k, n)), synth.int_inputs(85, (N, n))
