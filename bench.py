@@ -104,7 +104,8 @@ def parse():
                          "for profiling), then exit")
     ap.add_argument("--attn-prefill-only", type=int, default=0, metavar="CALLS",
                     help="only run the six attention-projection products of one Llama-3-70B rank at 4096 "
-                         "tokens (and the vendor BLAS on the same products) CALLS times (for profiling), then exit")
+                         "tokens (and the vendor BLAS on the same products and output dtypes) CALLS times (for "
+                         "profiling), then exit")
     ap.add_argument("--store-rate", action="store_true",
                     help="only run the store-throughput probe (one CU's fp32 / bf16 stores) and print its records")
     ap.add_argument("--mfma-rate", action="store_true",
@@ -177,17 +178,20 @@ def main() -> int:
         P, dX = torch.empty((Np, q.h), device=dev, dtype=f32), torch.empty((Np, q.h), device=dev, dtype=f32)
         dW, dWO = torch.empty((q.h, wq), device=dev, dtype=f32), torch.empty((wo, q.h), device=dev, dtype=f32)
         dO = torch.empty((Np, wo), device=dev, dtype=torch.bfloat16)
-        # the vendor BLAS on the same products, bf16 outputs, as plain NN
-        # products of contiguous operands (the transposes made beforehand)
+        # the vendor BLAS on the same products and output dtypes (fp32 where
+        # ours are fp32), as plain NN products of contiguous operands (the
+        # transposes made beforehand)
         Wrt, Xt, WOt, Ot = Wr.t().contiguous(), X.t().contiguous(), WO.t().contiguous(), O.t().contiguous()
-        vend = ((X, Wr), (O, WO), (dQ, Wrt), (Xt, dQ), (dY, WOt), (Ot, dY))
+        mm32, _ = mm_fp32_out(torch)
+        vend = ((torch.mm, X, Wr), (mm32, O, WO), (mm32, dQ, Wrt), (mm32, Xt, dQ), (torch.mm, dY, WOt),
+                (mm32, Ot, dY))
         for _ in range(args.attn_prefill_only):
             T.tp_col_linear(X, Wr, "none", Y=Y)
             T.tp_row_linear_partial(O, WO, P=P)
             T.tp_col_linear_bwd(X, Wr, dQ, dX_part=dX, dW=dW)
             T.tp_row_linear_bwd(O, WO, dY, dZ=dO, dW=dWO)
-            for a_, b_ in vend:
-                torch.matmul(a_, b_)
+            for mm_, a_, b_ in vend:
+                mm_(a_, b_)
         torch.cuda.synchronize()
         log(f"[bench] attention prefill products run {args.attn_prefill_only} times")
         return 0
@@ -352,6 +356,20 @@ def main() -> int:
     log(f"[bench] step {ms_step:.4f} ms  {value:.1f} TFLOP/s  "
         f"{100 * value / PEAK_BF16_TFLOPS:.1f}% of peak  (wall {wall:.3f}s)")
 
+    # The context rows are measured after the step: a Python-level failure in
+    # one of them (an error a call returns, a probe that cannot run) is
+    # recorded under rows["errors"] and the line is still printed.
+    errors = {}
+
+    def guarded(name, fn):
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001
+            import traceback
+            traceback.print_exc(file=sys.stderr)
+            errors[name] = f"{type(e).__name__}: {e}"[:400]
+            return None
+
     # ---------------- per-kernel timings (single-kernel entry points) ----------------
     # Each entry point below launches exactly the kernel (same template
     # instantiation and launch shape) that the step launches for that product.
@@ -429,6 +447,36 @@ def main() -> int:
                         args.reps)[0]
         kt["col_bwd_dx_8_chunks_then_dw"] = {"ms": round(ms_c8, 4), "unchunked_ms": round(ms_both, 4),
                                              "overhead": round(ms_c8 / ms_both - 1, 3)}
+    # The step's fp32 products against the vendor BLAS writing the same fp32
+    # outputs (torch.mm with fp32 output, transposed operands made contiguous
+    # outside the timing), side by side, three rounds in turn, medians
+    if not args.no_rows:
+        def fp32_side_by_side():
+            mm32, vout = mm_fp32_out(torch)
+            if not vout.startswith("fp32"):
+                return {"skipped": vout}
+            W_inT, XT, ZT = W_in.t().contiguous(), X.t().contiguous(), Z.t().contiguous()
+            pairs = {"gemm2_down_partial": (kern["gemm2_down_partial"], lambda: mm32(Z, W_out)),
+                     "bwd_dx_partial": (kern["bwd_dx_partial"], lambda: mm32(dH, W_inT)),
+                     "bwd_dw_gate_up": (kern["bwd_dw_gate_up"], lambda: mm32(XT, dH)),
+                     "bwd_dw_down": (kern["bwd_dw_down"], lambda: mm32(ZT, dY))}
+            rr = {k: ([], []) for k in pairs}
+            for _ in range(3):
+                for k, (ours, vend) in pairs.items():
+                    rr[k][0].append(time_fn(ours, args.reps)[1])
+                    rr[k][1].append(time_fn(vend, args.reps)[1])
+            del W_inT, XT, ZT
+            res = {}
+            for k, (o, v) in rr.items():
+                mo, mv = float(np.median(o)), float(np.median(v))
+                res[k] = {"ms": round(mo, 4), "vendor_fp32_out_ms": round(mv, 4),
+                          "ours_faster_by": round(mv / mo - 1, 3)}
+            log(f"[bench] fp32 products vs vendor BLAS with fp32 outputs: " +
+                ", ".join(f"{k} {v['ms']} vs {v['vendor_fp32_out_ms']}" for k, v in res.items()))
+            return res
+        sbs = guarded("vendor_fp32_side_by_side", fp32_side_by_side)
+        if sbs is not None:
+            kt["vendor_fp32_side_by_side"] = sbs
 
     # The fp32 epilogue's cost: GEMM2's output shape (512 tiles of 256 x 256,
     # two waves on 256 CUs) contracted over K = 64, two k32 sub-steps, so a
@@ -487,20 +535,6 @@ def main() -> int:
     rows["bwd_tflops"] = round(bwd_flops / (rows["bwd_ms"] * 1e-3) / 1e12, 1)
 
     del Z, H, P, dH, dX, dWi, dWo
-    # The context rows below are measured after the step: a Python-level
-    # failure in one of them (an error a call returns, a probe that cannot
-    # run) is recorded under rows["errors"] and the line is still printed.
-    errors = {}
-
-    def guarded(name, fn):
-        try:
-            return fn()
-        except Exception as e:  # noqa: BLE001
-            import traceback
-            traceback.print_exc(file=sys.stderr)
-            errors[name] = f"{type(e).__name__}: {e}"[:400]
-            return None
-
     if not args.no_rows:
         rows.update(guarded("rows", lambda: measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph,
                                                           args.reps)) or {})
@@ -636,22 +670,25 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
         T.tp_col_linear_bwd(X, W_r, dQKV, dX_part=dXq, dW=dWq)
         T.tp_row_linear_bwd(O, W_O, dY, dZ=dO, dW=dWO)
 
-    # The vendor BLAS (torch.matmul) on the same operands, bf16 outputs, as
-    # plain NN products of contiguous operands (the transposes made here, out
-    # of the timing). Both are timed side by side, three rounds in turn
-    # (medians): the chip's power state carries over from one measurement to
-    # the next, so only measurements taken together compare.
+    # The vendor BLAS (torch.mm) on the same operands, as plain NN products
+    # of contiguous operands (the transposes made here, out of the timing),
+    # writing the same output dtypes as ours (fp32 for W_O, dX, dW, dW_O;
+    # bf16 for QKV and dO) where torch offers fp32 outputs of bf16 products.
+    # Both are timed side by side, three rounds in turn (medians): the chip's
+    # power state carries over from one measurement to the next, so only
+    # measurements taken together compare.
     W_rT, W_OT, XT, OT = W_r.t().contiguous(), W_O.t().contiguous(), X.t().contiguous(), O.t().contiguous()
+    mm32, vendor_out = mm_fp32_out(torch)
 
     def vendor_fwd():
-        torch.matmul(X, W_r)
-        torch.matmul(O, W_O)
+        torch.mm(X, W_r)
+        mm32(O, W_O)
 
     def vendor_bwd():
-        torch.matmul(dQKV, W_rT)
-        torch.matmul(XT, dQKV)
-        torch.matmul(dY, W_OT)
-        torch.matmul(OT, dY)
+        mm32(dQKV, W_rT)
+        mm32(XT, dQKV)
+        torch.mm(dY, W_OT)
+        mm32(OT, dY)
 
     rounds = {k: [] for k in ("fwd", "vendor_fwd", "bwd", "vendor_bwd")}
     for _ in range(3):
@@ -663,7 +700,7 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
             "ms": round(ms, 4), "gflop": round(fl / 1e9, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
             "vendor_blas_ms": round(mv, 4), "vendor_blas_tflops": round(fl / (mv * 1e-3) / 1e12, 1),
             "rounds_ms": [round(x, 4) for x in rounds[k]],
-            "vendor_rounds_ms": [round(x, 4) for x in rounds["vendor_" + k]]}
+            "vendor_rounds_ms": [round(x, 4) for x in rounds["vendor_" + k]], "vendor_outputs": vendor_out}
     log(f"[bench] attention prefill, ours vs vendor BLAS side by side: fwd "
         f"{res['attn_proj_fwd_prefill']['ms']} vs {res['attn_proj_fwd_prefill']['vendor_blas_ms']} ms, bwd "
         f"{res['attn_proj_bwd_prefill']['ms']} vs {res['attn_proj_bwd_prefill']['vendor_blas_ms']} ms")
@@ -767,6 +804,20 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     res["gpt_gelu_mlp_fwd_t4"] = {"ms": round(ms, 4), "gflop": round(flg / 1e9, 2),
                                   "tflops": round(flg / (ms * 1e-3) / 1e12, 1)}
     return res
+
+
+def mm_fp32_out(torch):
+    """(mm, label): torch.mm writing fp32 outputs of a bf16 product when torch
+    offers it on this device (checked on a small product), else the bf16 one."""
+    try:
+        a = torch.ones((64, 64), dtype=torch.bfloat16, device="cuda:0")
+        c = torch.mm(a, a, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        if c.dtype == torch.float32 and float(c[0, 0]) == 64.0:
+            return (lambda x, y: torch.mm(x, y, out_dtype=torch.float32)), "fp32 where ours are fp32"
+    except (RuntimeError, TypeError):
+        pass
+    return (lambda x, y: torch.mm(x, y)), "bf16 (no fp32 outputs in this torch)"
 
 
 def vendor_reference(torch, dev, time_fn, reps, N, h, f):
