@@ -772,6 +772,50 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
                              "logit_bytes_not_written": 4 * lw.N * v_loc}
     res["lm_head_ce_bwd"] = {"ms": round(ms_b, 4), "gflop": round(3 * fl_ce / 1e9, 2),
                              "tflops": round(3 * fl_ce / (ms_b * 1e-3) / 1e12, 1)}
+    # The unfused alternative, timed side by side (three rounds in turn,
+    # medians): the vendor BLAS writes the fp32 logits, then eager torch
+    # takes each row's max, sum of exp(z - max) and target logit (forward);
+    # the backward recomputes the logits, forms (softmax - one-hot) * dloss in
+    # bf16 and runs dX and dW as vendor products with fp32 outputs.
+    try:
+        mm32, vout = mm_fp32_out(torch)
+        inr = (yl >= 0) & (yl < v_loc)
+        yc = yl.clamp(0, v_loc - 1).long()
+        rows_in = torch.arange(lw.N, device=dev)[inr]
+        cols_in = yc[inr]
+        minus1 = torch.tensor(-1.0, device=dev)
+        WlT, XlT = Wl.t().contiguous(), Xl.t().contiguous()
+
+        def vendor_ce_fwd():
+            z = mm32(Xl, Wl)
+            m = z.amax(dim=1)
+            torch.exp(z - m[:, None]).sum(dim=1)
+            torch.where(inr, z.gather(1, yc[:, None]).squeeze(1), 0.0)
+
+        def vendor_ce_bwd():
+            z = mm32(Xl, Wl)
+            pz = torch.exp(z - m_ce.reshape(-1, 1)) / S_ce.reshape(-1, 1)
+            pz.index_put_((rows_in, cols_in), minus1, accumulate=True)
+            dz = (pz * dlo.reshape(-1, 1)).to(bf)
+            mm32(dz, WlT)
+            mm32(XlT, dz)
+
+        rr = {k: [] for k in ("fwd", "vfwd", "bwd", "vbwd")}
+        for _ in range(3):
+            for k, fn in (("fwd", ce_fwd), ("vfwd", vendor_ce_fwd), ("bwd", ce_bwd), ("vbwd", vendor_ce_bwd)):
+                rr[k].append(time_fn(fn, reps)[1])
+        res["lm_head_ce_fwd"].update({"side_by_side_ms": round(float(np.median(rr["fwd"])), 4),
+                                      "vendor_unfused_ms": round(float(np.median(rr["vfwd"])), 4),
+                                      "vendor_outputs": vout})
+        res["lm_head_ce_bwd"].update({"side_by_side_ms": round(float(np.median(rr["bwd"])), 4),
+                                      "vendor_unfused_ms": round(float(np.median(rr["vbwd"])), 4),
+                                      "vendor_outputs": vout})
+        log(f"[bench] LM head + CE, fused vs vendor unfused side by side: fwd "
+            f"{res['lm_head_ce_fwd']['side_by_side_ms']} vs {res['lm_head_ce_fwd']['vendor_unfused_ms']} ms, bwd "
+            f"{res['lm_head_ce_bwd']['side_by_side_ms']} vs {res['lm_head_ce_bwd']['vendor_unfused_ms']} ms")
+        del WlT, XlT
+    except Exception as e:  # noqa: BLE001  (context only: the fused rows above stand)
+        res["lm_head_ce_fwd"]["vendor_unfused_error"] = f"{type(e).__name__}: {e}"[:300]
     del Xl, Wl, dZl, dXl, dWl, stats
 
     # --- Llama-3-70B vocab-parallel input embedding, one shard of 8 (rank 0) ---
@@ -790,6 +834,37 @@ def measure_rows(T, synth, np, torch, dev, to_dev, time_fn, time_graph, reps):
     eb = 4 * lw.h * (in_range + v_loc)  # gradient rows read + every table row written
     res["embed_bwd"] = {"ms": round(ms, 5), "bytes": eb, "gbs": round(eb / (ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(eb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+    # The same two steps in eager torch, timed side by side (three rounds in
+    # turn, medians): a masked F.embedding for the lookup, a zeroed fp32 table
+    # with index_add_ of the in-range tokens' gradient rows for the gradient.
+    try:
+        inr_e = (idl >= 0) & (idl < v_loc)
+        idc = idl.clamp(0, v_loc - 1).long()
+        tok_in = torch.arange(lw.N, device=dev)[inr_e]
+        id_in = idc[inr_e]
+        dY_in = dYe[tok_in].contiguous()
+
+        def torch_embed_fwd():
+            torch.where(inr_e[:, None], torch.nn.functional.embedding(idc, El), 0.0)
+
+        def torch_embed_bwd():
+            torch.zeros((v_loc, lw.h), dtype=f32, device=dev).index_add_(0, id_in, dY_in)
+
+        rr = {k: [] for k in ("fwd", "tfwd", "bwd", "tbwd")}
+        for _ in range(3):
+            rr["fwd"].append(time_graph(lambda: T.tp_vocab_embed_fwd(idl, El, 0, out=outl), 16))
+            rr["tfwd"].append(time_graph(torch_embed_fwd, 16))
+            rr["bwd"].append(time_fn(lambda: T.tp_vocab_embed_bwd(idl, dYe, 0, v_loc, dE_i=dEl), reps)[1])
+            rr["tbwd"].append(time_fn(torch_embed_bwd, reps)[1])
+        for k in ("fwd", "bwd"):
+            res[f"embed_{k}"].update({"side_by_side_ms": round(float(np.median(rr[k])), 5),
+                                      "torch_eager_ms": round(float(np.median(rr["t" + k])), 5)})
+        log(f"[bench] embedding vs eager torch side by side: fwd {res['embed_fwd']['side_by_side_ms']} vs "
+            f"{res['embed_fwd']['torch_eager_ms']} ms, bwd {res['embed_bwd']['side_by_side_ms']} vs "
+            f"{res['embed_bwd']['torch_eager_ms']} ms")
+        del dY_in
+    except Exception as e:  # noqa: BLE001  (context only: the rows above stand)
+        res["embed_fwd"]["torch_eager_error"] = f"{type(e).__name__}: {e}"[:300]
     del El, outl, dYe, dEl
 
     # --- GPT-style GeLU MLP shard, t = 4, forward ---

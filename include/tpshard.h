@@ -27,7 +27,7 @@
  *              tokens, or a narrow shard such as the attention projections')
  *              splits K over workgroups and sums their f32 partials in a
  *              second kernel; tp_vocab_ce_fwd keeps per-tile records and
- *              tp_vocab_embed_bwd per-row stamps. That scratch is device
+ *              tp_vocab_embed_bwd per-row flags. That scratch is device
  *              memory the caller provides: every call that may need it takes
  *              (void* workspace, size_t workspace_bytes), and the host-only
  *              query of the same name plus "_workspace_size", given the same
@@ -53,8 +53,8 @@
  *              is enqueued, a status != TP_OK is returned and a message is
  *              kept in thread-local storage (tp_last_error). Calls are
  *              re-entrant across threads (the library holds no state besides
- *              each thread's last error message and a counter of
- *              tp_vocab_embed_bwd calls).
+ *              each thread's last error message, each device's CU count and
+ *              the address of each device's array of tp_col_linear_noalloc).
  *   {U}:       an f32 output marked {U} is a partial sum ("unreduced" in
  *              [TPSP]/[SB6] notation): the full result is the sum of the t
  *              ranks' outputs. The exchange that sums them (an all-reduce) is
@@ -382,8 +382,9 @@ tp_status tp_vocab_embed_fwd(const int32_t* ids, const void* E_i, int64_t vocab_
  * Its backward: dE_i f32 [v_loc, h], row v = the sum of dY[n] over the tokens
  * n whose id is vocab_start + v, added in token order (deterministic); rows
  * no token uses are zero. dY f32 [N, h]. h <= 16384 (else UNSUPPORTED).
- * Its workspace holds a 4-byte stamp per table row (v_loc * 4 bytes); any
- * earlier contents are fine.
+ * Its workspace holds a row count, a flag per table row and a list of the
+ * rows the tokens use: 4 * (1 + v_loc + min(N, v_loc)) bytes rounded up to
+ * 16, cleared by the call itself (any earlier contents are fine).
  */
 tp_status tp_vocab_embed_bwd_workspace_size(int64_t N, int64_t v_loc, int64_t h,
                                             size_t* bytes);

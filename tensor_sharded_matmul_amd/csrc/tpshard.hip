@@ -511,53 +511,64 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restric
     }
 }
 
-// Vocab-parallel embedding, backward: one workgroup per table row v, its h
-// columns spread over the 256 threads (4 columns per thread per 1024, held
-// in registers). The ids are scanned in chunks of 256, 16 chunks of ids
-// loaded into registers at a time; a chunk's tokens whose id is
-// vocab_start + v are listed in ascending order (a wave ballot per 64 ids,
-// the four waves' matches placed by prefix counts in LDS) and their gradient
-// rows added in that order. Masks and lists alternate between two LDS
-// buffers, so a chunk without a match costs one barrier. Every row's sum is
-// taken in token order: the result does not depend on scheduling.
-// Most rows of a shard receive no token (4096 tokens over Llama-3's 128256
-// ids put about 512 into a shard's 16128 rows), and for those the scan is
-// wasted: a first kernel stamps every row some token uses with this call's
-// number, and a row whose stamp differs writes its zeros without scanning.
-// The stamps live in the stream's workspace, whose other users leave
-// arbitrary bits there; a stale or accidental match only costs a scan that
-// finds nothing, so the result never depends on the stamps' earlier
-// contents.
+// Vocab-parallel embedding, backward, in three kernels. Most rows of a shard
+// receive no token (4096 tokens over Llama-3's 128256 ids put about 512 into
+// a shard's 16128 rows), so the table gradient is mostly its zeros:
+//  1. embed_clear_kernel clears the call's bookkeeping in the workspace: a
+//     row count, one flag per table row and a list of rows.
+//  2. embed_fill_mark_kernel stores the zeros of the whole table, one 16-byte
+//     unit per thread in address order (the rate of a plain fill, every
+//     store independent of any load), and its first threads mark the rows
+//     the tokens use: the first token to flag a row (an atomic exchange)
+//     appends it to the list (an atomic counter).
+//  3. embed_rows_kernel gives each listed row a workgroup that sums the
+//     gradient rows of the tokens whose id is vocab_start + v, in token
+//     order, and overwrites the row's zeros.
+// A row's h columns are spread over the 256 threads of its workgroup (4
+// columns per thread per 1024, held in registers). The ids are scanned in
+// chunks of 256, 16 chunks of ids loaded into registers at a time; a chunk's
+// matching tokens are listed in ascending order (a wave ballot per 64 ids,
+// the four waves' matches placed by prefix counts in LDS) and their rows
+// added in that order. Masks and lists alternate between two LDS buffers, so
+// a chunk without a match costs one barrier. Every row's sum is taken in
+// token order: the result does not depend on scheduling or on the order of
+// the list. The bookkeeping is cleared by every call, so the workspace's
+// earlier contents never matter. (One workgroup per table row, storing its
+// zeros or its sum, took 113-116 us on the Llama-3-70B shard: its register
+// use, set by the summing path, limits the stores in flight.)
 constexpr int kEmbedMaxH = 16384;
 
-__global__ void __launch_bounds__(256) embed_mark_kernel(const int32_t* __restrict__ ids, int64_t vocab_start,
-                                                         int64_t N, int v_loc, uint32_t* __restrict__ stamp,
-                                                         uint32_t cur) {
-    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < N; n += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t v = (int64_t)ids[n] - vocab_start;
-        if (v >= 0 && v < v_loc) stamp[v] = cur;  // every writer of a row writes the same value
+__global__ void __launch_bounds__(256) embed_clear_kernel(uint32_t* __restrict__ ws, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        ws[i] = 0u;
+}
+
+__global__ void __launch_bounds__(256) embed_fill_mark_kernel(float* __restrict__ dE, int64_t units,
+                                                              const int32_t* __restrict__ ids, int64_t vocab_start,
+                                                              int64_t N, int v_loc, uint32_t* __restrict__ count,
+                                                              uint32_t* __restrict__ used,
+                                                              uint32_t* __restrict__ list) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < units) reinterpret_cast<f32x4_t*>(dE)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (i < N) {
+        const int64_t v = (int64_t)ids[i] - vocab_start;
+        if (v >= 0 && v < v_loc && atomicExch(&used[v], 1u) == 0u) list[atomicAdd(count, 1u)] = (uint32_t)v;
     }
 }
 
-__global__ void __launch_bounds__(256) embed_bwd_kernel(const int32_t* __restrict__ ids,
-                                                        const float* __restrict__ dY, int64_t vocab_start,
-                                                        int N, int h, float* __restrict__ dE,
-                                                        const uint32_t* __restrict__ stamp, uint32_t cur) {
+// Row `target - vocab_start` of dE: the sum, in token order, of the dY rows
+// of the tokens whose id is `target` (the whole workgroup; chunk numbers
+// continue from one row to the next so that the LDS buffers keep
+// alternating).
+__device__ __forceinline__ void embed_row_sum(const int32_t* __restrict__ ids, const float* __restrict__ dY,
+                                              int64_t target, int N, int h, float* __restrict__ row,
+                                              int (&list)[2][256], uint64_t (&masks)[2][4], int& chunk, int tid,
+                                              int lane, int wave) {
     constexpr int Q = kEmbedMaxH / 1024;  // column quads per thread
     constexpr int U = 16;                 // id chunks loaded at a time
-    __shared__ int list[2][256];
-    __shared__ uint64_t masks[2][4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t target = vocab_start + blockIdx.x;
-    if (stamp[blockIdx.x] != cur) {  // no token uses this row (uniform)
-        float* row = dE + (int64_t)blockIdx.x * h;
-        for (int c = tid * 4; c < h; c += 1024) *reinterpret_cast<f32x4_t*>(row + c) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        return;
-    }
     f32x4_t acc[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int chunk = 0;
     for (int g = 0; g < N; g += 256 * U) {
         int my[U];
 #pragma unroll
@@ -591,11 +602,26 @@ __global__ void __launch_bounds__(256) embed_bwd_kernel(const int32_t* __restric
             }
         }
     }
-    float* row = dE + (int64_t)blockIdx.x * h;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int c = q * 1024 + tid * 4;
         if (c < h) *reinterpret_cast<f32x4_t*>(row + c) = acc[q];
+    }
+}
+
+__global__ void __launch_bounds__(256) embed_rows_kernel(const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ dY, int64_t vocab_start, int N,
+                                                         int h, float* __restrict__ dE,
+                                                         const uint32_t* __restrict__ count,
+                                                         const uint32_t* __restrict__ list) {
+    __shared__ int lst[2][256];
+    __shared__ uint64_t masks[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rows = (int)*count;  // the same in every thread: the loop below is uniform
+    int chunk = 0;
+    for (int b = blockIdx.x; b < rows; b += gridDim.x) {
+        const int v = (int)list[b];
+        embed_row_sum(ids, dY, vocab_start + v, N, h, dE + (int64_t)v * h, lst, masks, chunk, tid, lane, wave);
     }
 }
 
@@ -951,7 +977,8 @@ static tp_status embed_bwd_plan(const char* fn, int64_t N, int64_t v_loc, int64_
     TP_TRY(check_embed(fn, N, v_loc, h, vocab_start));
     if (h > kEmbedMaxH) return fail(TP_ERR_UNSUPPORTED, "%s: h = %lld above %d", fn, (long long)h, kEmbedMaxH);
     if (N > 0x7fffffffLL) return fail(TP_ERR_UNSUPPORTED, "%s: too many tokens", fn);
-    need = (size_t)v_loc * sizeof(uint32_t);  // one stamp per table row
+    // a row count, a flag per table row, a list of at most min(N, v_loc) rows
+    need = ((size_t)(1 + v_loc + std::min(N, v_loc)) * sizeof(uint32_t) + 15) / 16 * 16;
     return TP_OK;
 }
 
@@ -1442,17 +1469,18 @@ tp_status tp_vocab_embed_bwd(const int32_t* ids, const float* dY, int64_t vocab_
     TP_CHECK_PTR(dE_i, "dE_i");
     TP_TRY(check_workspace(fn, {workspace, workspace_bytes}, need));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint32_t* stamp = static_cast<uint32_t*>(workspace);
-    static std::atomic<uint32_t> g_stamp{0};
-    uint32_t cur = ++g_stamp;
-    if (cur == 0) cur = ++g_stamp;  // after 2^32 calls; any value works, see the kernels
-    if (N > 0) {
-        const unsigned mark_blocks = (unsigned)std::min<int64_t>((N + 255) / 256, 1024);
-        hipLaunchKernelGGL(embed_mark_kernel, dim3(mark_blocks), dim3(256), 0, s, ids, vocab_start, N, (int)v_loc,
-                           stamp, cur);
-    }
-    hipLaunchKernelGGL(embed_bwd_kernel, dim3((unsigned)v_loc), dim3(256), 0, s, ids, dY, vocab_start, (int)N,
-                       (int)h, dE_i, stamp, cur);
+    uint32_t* count = static_cast<uint32_t*>(workspace);
+    uint32_t* used = count + 1;
+    uint32_t* list = used + v_loc;
+    const int64_t words = 1 + v_loc;  // the list needs no clearing: only its first *count entries are read
+    hipLaunchKernelGGL(embed_clear_kernel, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 1024)), dim3(256),
+                       0, s, count, words);
+    const int64_t units = v_loc * h / 4;  // 16-byte units of the table (h is a multiple of 64)
+    hipLaunchKernelGGL(embed_fill_mark_kernel, dim3((unsigned)((std::max(units, N) + 255) / 256)), dim3(256), 0, s,
+                       dE_i, units, ids, vocab_start, N, (int)v_loc, count, used, list);
+    if (N > 0)
+        hipLaunchKernelGGL(embed_rows_kernel, dim3((unsigned)std::min<int64_t>(std::min(N, v_loc), 1024)),
+                           dim3(256), 0, s, ids, dY, vocab_start, (int)N, (int)h, dE_i, count, list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

@@ -153,7 +153,7 @@ def test_gemm_entry_points_validate_before_launch():
 
 # Every call that may need scratch memory, with sizes that need some at the
 # Llama-3-70B t = 8 shapes (decode-sized token counts; the narrow attention
-# shards; the cross-entropy records; the embedding stamps) and the arguments
+# shards; the cross-entropy records; the embedding bookkeeping) and the arguments
 # of its workspace query.
 WS_CASES = {
     "tp_col_linear": (16, 8192, 1280, 0),
@@ -186,8 +186,8 @@ def test_workspace_query_values():
     # the split-K decode product: ksplit partials of [N, n] f32; the
     # cross-entropy records: one per 64 vocab columns per token (256 x 256
     # ping-pong tiles), or one per 112 when the weight's window needs 64-bit
-    # offsets (256 x 224 tiles), 12 bytes each; the embedding stamps: 4 bytes
-    # per table row
+    # offsets (256 x 224 tiles), 12 bytes each; the embedding bookkeeping: a
+    # count, a flag per table row and a list of at most min(N, v_loc) rows
     n = T.workspace_size("tp_col_linear", 16, 8192, 1280, 0)
     assert n % (16 * 1280 * 4) == 0 and 2 <= n // (16 * 1280 * 4) <= 64
     # decode plans (256 CUs): 32-column slabs when no K split is needed (at
@@ -205,7 +205,9 @@ def test_workspace_query_values():
     # (8192 + 512) * 131072 * 2 >= 2^31: a 131072-wide vocabulary shard
     assert T.workspace_size("tp_vocab_ce_fwd", 64, 8192, 131072) == 64 * 2 * -(-131072 // 224) * 12
     assert T.workspace_size("tp_vocab_ce_fwd", 64, 8192, 123200) == 64 * 4 * -(-123200 // 256) * 12
-    assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == 16128 * 4
+    r16 = lambda b: (b + 15) // 16 * 16  # noqa: E731
+    assert T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192) == r16((1 + 16128 + 4096) * 4)
+    assert T.workspace_size("tp_vocab_embed_bwd", 100000, 16128, 8192) == r16((1 + 2 * 16128) * 4)
     # a weight gradient on TN mid tiles (2112 x 1984 over 3000 tokens: 136
     # tiles of 128 x 256, 72 of 256 x 256) is not split, and dZ of the same
     # call contracts over K = 1984 < 2048 without a split: no workspace
@@ -248,7 +250,8 @@ def test_too_small_workspace_is_rejected_before_launch():
     assert col(p, p, p, 16, 8192, 1280, 0, NULL, ctypes.c_void_p(0x10008), need, NULL) == 1
     assert "aligned" in T.tp_last_error()
     emb = _raw("tp_vocab_embed_bwd")
-    assert emb(p, p, 0, 4096, 16128, 8192, p, p, 16128 * 4 - 1, NULL) == 1
+    need_e = T.workspace_size("tp_vocab_embed_bwd", 4096, 16128, 8192)
+    assert emb(p, p, 0, 4096, 16128, 8192, p, p, need_e - 1, NULL) == 1
 
 
 def test_noalloc_entry_point_validates_before_launch():
