@@ -115,6 +115,10 @@ def parse():
                     help="only run the chunked schedule on the Llama-3-70B MLP shard CALLS times: GEMM2 in 1, 2, "
                          "4 and 8 token-row chunks, dX_part in 1, 2, 4 and 8 chunks, then dX_part in 8 chunks "
                          "followed by dW_gate|up (for profiling), then exit")
+    ap.add_argument("--embed-only", type=int, default=0, metavar="CALLS",
+                    help="only run the vocab-parallel embedding of one Llama-3-70B rank (16128 rows, 4096 tokens) "
+                         "forward and backward CALLS times, then eager torch's lookup and zeroed table + "
+                         "index_add_ CALLS times (for profiling), then exit")
     ap.add_argument("--decode-only", type=int, default=0, metavar="CALLS",
                     help="only run the decode-sized (16 tokens) QKV and W_O products of the Llama-3-70B "
                          "attention shard CALLS times (16 rotated weight copies; for profiling), then exit")
@@ -213,6 +217,28 @@ def main() -> int:
             T.tp_col_linear_bwd_chunked(Xc, Wg, dHc, 8, dX_part=dXc, dW=dWc, events=evs[8])
         torch.cuda.synchronize()
         log(f"[bench] chunked schedule run {args.chunked_only} times")
+        return 0
+    if args.embed_only:
+        lw = synth.WORKLOADS["llama70b_lm_head_t8"]
+        v_loc = lw.extra["V_pad"] // lw.t
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(lw.seed + 1)
+        E = torch.randn((v_loc, lw.h), device=dev, generator=gen).to(torch.bfloat16)
+        ids = torch.randint(0, lw.extra["V"], (lw.N,), device=dev, generator=gen, dtype=torch.int32)
+        dYe = torch.randn((lw.N, lw.h), device=dev, generator=gen)
+        out = torch.empty((lw.N, lw.h), dtype=torch.bfloat16, device=dev)
+        dE = torch.empty((v_loc, lw.h), dtype=torch.float32, device=dev)
+        inr = (ids >= 0) & (ids < v_loc)
+        idc = ids.clamp(0, v_loc - 1).long()
+        id_in, dY_in = idc[inr], dYe[inr].contiguous()
+        for _ in range(args.embed_only):
+            T.tp_vocab_embed_fwd(ids, E, 0, out=out)
+            T.tp_vocab_embed_bwd(ids, dYe, 0, v_loc, dE_i=dE)
+        for _ in range(args.embed_only):
+            torch.where(inr[:, None], torch.nn.functional.embedding(idc, E), 0.0)
+            torch.zeros((v_loc, lw.h), dtype=torch.float32, device=dev).index_add_(0, id_in, dY_in)
+        torch.cuda.synchronize()
+        log(f"[bench] embedding run {args.embed_only} times")
         return 0
     if args.decode_only:
         q = synth.WORKLOADS["llama70b_qkv_t8"]
